@@ -1,0 +1,208 @@
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one fa_fwd call (the whole fused forward pass: scores, online
+softmax, P.V, normalisation, lse) over the workload's seeded inputs, which are
+resident in device memory before timing starts.  Prints one JSON line.
+
+Reported alongside the throughput:
+  * roofline: the attention kernel against the dense fp16/bf16 MFMA peak,
+    with achieved = algorithmic FLOP per launch / mean launch time measured
+    with HIP events on the launch stream over the timed region; traffic =
+    HBM bytes per launch from rocprofv3 counters when they were taken on the
+    current kernel source (else null);
+  * cpu_baseline: the float64 oracle timed on this host's cores over a
+    bounded sample of the same workload's rows;
+  * a sampled parity check of the timed output against the oracle.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fa_inputs as fi  # noqa: E402
+
+# MI355X dense MFMA peak for fp16/bf16: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
+PEAK_TFLOPS_F16 = 2516.6
+KERNEL_SRC = os.path.join(ROOT, "tile_level_programming_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch measured by rocprofv3 on this kernel source, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, seconds: float, threads: int):
+    import oracle
+
+    per_row_flop = 4 * w.D * (w.unmasked_pairs() / w.Sq)  # algorithmic FLOP per query row, on average
+    rng = np.random.default_rng(1234)
+    total_rows = w.B * w.H * w.Sq
+    # grow a calibration batch until it takes >= 1 s, then size the timed
+    # sample to about `seconds` of work
+    n = threads * 4
+    while True:
+        rows = rng.integers(0, total_rows, n)
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, w.dtype, w.scale, w.causal, rows, threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= 1.0 or n >= total_rows:
+            break
+        n *= 4
+    n = int(max(threads, min(total_rows, n * seconds / max(dt, 1e-6))))
+    rows = rng.integers(0, total_rows, n)
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, w.dtype, w.scale, w.causal, rows, threads=threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(n * per_row_flop / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n} seeded random query rows of {w.name} ({n / total_rows:.2%} of the rows), "
+                  f"float64, explicit scores over all {w.Sk} keys per row, {dt:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=fi.HEADLINE, choices=list(fi.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention path shards over (batch, head) with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tile_level_programming_amd import fa
+
+    w = fi.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: generating seeded inputs")
+    q, k, v = fi.make_inputs(w)
+    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    dt_code = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
+    call_args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 w.B, w.H, w.Sq, w.Sk, w.D, float(w.scale), int(w.causal), dt_code, sp)
+
+    def step():
+        st = fa.fa_fwd(*call_args)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms = ms_total / args.steps
+    flop = w.flops()
+    tflops = flop / (ms * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s (wall {wall:.3f} s)")
+
+    # sampled parity of the timed output
+    import oracle
+
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, w.B * w.H * w.Sq - 1], rng.integers(0, w.B * w.H * w.Sq, 62)]))
+    idx = torch.from_numpy(rows).to(dev)
+    o_s = o.view(-1, w.D)[idx].double().cpu().numpy()
+    l_s = lse.view(-1)[idx].double().cpu().numpy()
+    threads = min(16, os.cpu_count() or 1)
+    o_ref, l_ref = oracle.attention_rows(q, k, v, w.dtype, w.scale, w.causal, rows, threads=threads)
+    err_o = float(np.abs(o_s - o_ref).max())
+    err_l = float((np.abs(l_s - l_ref) / np.maximum(np.abs(l_ref), 1.0)).max())
+    tol_o = 5e-3 if w.dtype == "f16" else 2e-2
+    parity_ok = bool(err_o <= tol_o and err_l <= 1e-3 and np.isfinite(o_s).all())
+    log(f"[bench] sampled parity: max|dO|={err_o:.2e} lse_rel={err_l:.2e} ok={parity_ok}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {threads} threads, ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds, threads)
+
+    traffic = traffic_for(w.name)
+    line = {
+        "metric": "attention fwd TFLOP/s and % of MI355X dense fp16/bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded i.i.d. normal Q, K, V)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "D": w.D,
+                   "causal": w.causal, "scale": w.scale, "algorithmic_flop": flop,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS_F16, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_F16,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS_F16, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "parity_sample": {"rows": int(rows.size), "max_abs_err_o": err_o, "max_rel_err_lse": err_l,
+                          "ok": parity_ok},
+        "kernel_sha256_16": kernel_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

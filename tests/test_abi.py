@@ -1,0 +1,82 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device (these
+calls return before any HIP call, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "for", "return")))
+
+
+@pytest.fixture(scope="module")
+def fa():
+    from tile_level_programming_amd import fa as mod
+
+    return mod
+
+
+def test_header_declares_entry_points():
+    assert _declared_functions() == ["fa_fwd", "fa_status_string"]
+
+
+def test_library_exports_every_declared_symbol(fa):
+    lib = fa.library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_total(fa):
+    for st in (0, 1, 2, 3, -1, 4, 1000):
+        s = fa.fa_status_string(st)
+        assert isinstance(s, str) and s
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+A = 1 << 20  # a fake, 16-byte aligned, never dereferenced device address
+
+
+def _call(fa, **kw):
+    args = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, Sq=16, Sk=16, D=64,
+                scale=0.125, causal=0, dtype=fa.FA_F16, stream=0)
+    args.update(kw)
+    return fa.fa_fwd(**args)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(lse=0),
+    dict(q=A + 8), dict(k=2 * A + 2), dict(v=3 * A + 4), dict(o=4 * A + 1), dict(lse=5 * A + 2),
+    dict(B=0), dict(H=0), dict(Sq=0), dict(Sk=0), dict(B=-1), dict(D=0),
+    dict(scale=float("inf")), dict(scale=float("nan")), dict(scale=float("-inf")),
+    dict(Sq=1 << 25, D=64), dict(Sk=1 << 24, D=128), dict(B=1 << 16, H=1 << 16),
+    dict(o=A), dict(o=3 * A + 512), dict(lse=2 * A), dict(lse=4 * A + 256),
+])
+def test_invalid_arguments(fa, kw):
+    assert _call(fa, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(D=32), dict(D=96), dict(D=256), dict(dtype=2), dict(dtype=-1)])
+def test_unsupported(fa, kw):
+    assert _call(fa, **kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    import importlib
+
+    from tile_level_programming_amd import fa as mod
+
+    monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        mod._load()

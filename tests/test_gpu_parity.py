@@ -1,0 +1,255 @@
+"""GPU parity of the HIP attention forward pass against the float64 oracle.
+
+All calls go through the C ABI (via the ctypes binding).  Inputs are the
+seeded bit patterns of ``fa_inputs``; the oracle consumes the same bits.
+
+Tolerances (the acceptance bar of the port): max |O - O_ref| <= 5e-3 for
+fp16 and <= 2e-2 for bf16; |lse - lse_ref| / max(|lse_ref|, 1) <= 1e-3.  The
+guarded denominator keeps the lse bound meaningful for rows whose lse is near
+zero (e.g. the first causal row, whose lse is a single logit).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f16": 5e-3, "bf16": 2e-2}
+TOL_LSE = 1e-3
+THREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def fa():
+    from tile_level_programming_amd import fa as mod
+
+    return mod
+
+
+def to_dev(torch, bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    t = t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+    return t.cuda()
+
+
+def to_f64(torch, t):
+    return t.float().double().cpu().numpy()
+
+
+def run_gpu(torch, fa, q, k, v, dtype, scale, causal, prefill=float("nan")):
+    qd, kd, vd = (to_dev(torch, x, dtype) for x in (q, k, v))
+    o = torch.full_like(qd, prefill)
+    lse = torch.full(qd.shape[:3], prefill, dtype=torch.float32, device=qd.device)
+    fa.fwd(qd, kd, vd, causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite O"
+    assert np.all(np.isfinite(lse_gpu)), f"{what}: non-finite lse"
+    err_o = np.abs(o_gpu - o_ref)
+    i = np.unravel_index(np.argmax(err_o), err_o.shape)
+    assert err_o.max() <= TOL_O[dtype], f"{what}: max |dO| {err_o.max():.3e} at {i}"
+    err_l = np.abs(lse_gpu - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)
+    j = np.unravel_index(np.argmax(err_l), err_l.shape)
+    assert err_l.max() <= TOL_LSE, f"{what}: max lse err {err_l.max():.3e} at {j}"
+    return float(err_o.max()), float(err_l.max())
+
+
+def full_check(torch, fa, oracle_mod, q, k, v, dtype, scale, causal, what=""):
+    o, lse = run_gpu(torch, fa, q, k, v, dtype, scale, causal)
+    o_ref, lse_ref = oracle_mod.attention(q, k, v, dtype, scale, causal, threads=THREADS)
+    return check(to_f64(torch, o), lse.double().cpu().numpy(), o_ref, lse_ref, dtype, what)
+
+
+def sample_rows(w, n_random=384, seed=0):
+    """Rows the oracle evaluates one by one at full size: the first and last
+    rows of several heads, rows either side of every 64- and 128-row block
+    boundary in a few places, and seeded random rows over all heads."""
+    rng = np.random.default_rng(seed)
+    BH, S = w.B * w.H, w.Sq
+    heads = sorted(set([0, BH - 1, BH // 2] + list(rng.integers(0, BH, 3))))
+    local = set([0, 1, 2, 3, 31, 32, 63, 64, 127, 128, 129, 255, 256, S - 1, S - 2, S - 64, S - 129])
+    local |= set(int(x) for x in rng.integers(0, S, 16))
+    rows = [h * S + i for h in heads for i in sorted(local) if 0 <= i < S]
+    rows += list(rng.integers(0, BH * S, n_random))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+# --- the five measured shapes (six runs) -------------------------------------
+
+
+@pytest.mark.parametrize("name", list(fi.WORKLOADS))
+def test_workload_parity(torch_dev, fa, oracle_mod, name):
+    torch = torch_dev
+    w = fi.WORKLOADS[name]
+    print(f"[parity] {name}", flush=True)
+    q, k, v = fi.make_inputs(w)
+    if w.flops() <= 5e9:
+        full_check(torch, fa, oracle_mod, q, k, v, w.dtype, w.scale, w.causal, name)
+        return
+    o, lse = run_gpu(torch, fa, q, k, v, w.dtype, w.scale, w.causal)
+    o = o.view(-1, w.D)
+    lse = lse.view(-1)
+    # every output written and finite
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), name
+    rows = sample_rows(w)
+    idx = torch.from_numpy(rows).cuda()
+    o_s = to_f64(torch, o[idx])
+    l_s = lse[idx].double().cpu().numpy()
+    o_ref, l_ref = oracle_mod.attention_rows(q, k, v, w.dtype, w.scale, w.causal, rows, threads=THREADS)
+    check(o_s, l_s, o_ref, l_ref, w.dtype, name)
+
+
+# --- ragged and odd shapes ---------------------------------------------------
+
+ODD = [
+    # (B, H, Sq, Sk, D)
+    (1, 1, 1, 1, 64), (1, 2, 17, 17, 64), (2, 1, 77, 200, 128), (1, 1, 200, 77, 64),
+    (1, 3, 1000, 1000, 128), (1, 1, 129, 1, 64), (1, 1, 1, 1000, 128), (2, 2, 255, 257, 64),
+    (1, 1, 64, 64, 128), (1, 1, 1000, 17, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", ODD)
+def test_odd_shapes(torch_dev, fa, oracle_mod, shape, causal, dtype):
+    B, H, Sq, Sk, D = shape
+    seed = 100 + Sq + 7 * Sk
+    q = fi.tensor_bits(seed, "q", (B, H, Sq, D), dtype)
+    k = fi.tensor_bits(seed, "k", (B, H, Sk, D), dtype)
+    v = fi.tensor_bits(seed, "v", (B, H, Sk, D), dtype)
+    full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(D), causal, f"{shape} {causal} {dtype}")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1.0, 3.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scales(torch_dev, fa, oracle_mod, scale, causal):
+    dtype = "f16"
+    q = fi.tensor_bits(21, "q", (1, 2, 300, 64), dtype)
+    k = fi.tensor_bits(21, "k", (1, 2, 300, 64), dtype)
+    v = fi.tensor_bits(21, "v", (1, 2, 300, 64), dtype)
+    full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, scale, causal, f"scale {scale}")
+
+
+def test_large_logits_rescaling(torch_dev, fa, oracle_mod):
+    # sigma 4 inputs at D=128: logits with spread ~ 16*sqrt(128)/sqrt(128) ... large
+    # running-max jumps in every tile
+    dtype = "bf16"
+    q = fi.tensor_bits(22, "q", (1, 2, 600, 128), dtype, 4.0)
+    k = fi.tensor_bits(22, "k", (1, 2, 600, 128), dtype, 4.0)
+    v = fi.tensor_bits(22, "v", (1, 2, 600, 128), dtype)
+    for causal in (False, True):
+        full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(128), causal, "sigma4")
+
+
+# --- properties checkable without the oracle ---------------------------------
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_q_gives_prefix_mean(torch_dev, fa, causal):
+    torch = torch_dev
+    dtype = "f16"
+    Sq = Sk = 333
+    q = np.zeros((1, 1, Sq, 64), np.uint16)
+    k = fi.tensor_bits(23, "k", (1, 1, Sk, 64), dtype)
+    v = fi.tensor_bits(23, "v", (1, 1, Sk, 64), dtype)
+    o, lse = run_gpu(torch, fa, q, k, v, dtype, 0.125, causal)
+    vv = to_f64(torch, to_dev(torch, v, dtype))[0, 0]
+    n = np.arange(1, Sq + 1) if causal else np.full(Sq, Sk)
+    mean = np.cumsum(vv, axis=0) / np.arange(1, Sk + 1)[:, None] if causal else np.broadcast_to(vv.mean(0), (Sq, 64))
+    np.testing.assert_allclose(to_f64(torch, o)[0, 0], mean, atol=TOL_O[dtype])
+    np.testing.assert_allclose(lse.double().cpu().numpy()[0, 0], np.log(n), rtol=1e-5, atol=1e-5)
+
+
+def test_constant_v(torch_dev, fa):
+    torch = torch_dev
+    for dtype in ("f16", "bf16"):
+        q = fi.tensor_bits(24, "q", (1, 2, 257, 128), dtype, 2.0)
+        k = fi.tensor_bits(24, "k", (1, 2, 257, 128), dtype, 2.0)
+        row = fi.tensor_bits(24, "v", (1, 2, 1, 128), dtype)
+        v = np.ascontiguousarray(np.broadcast_to(row, (1, 2, 257, 128)))
+        o, _ = run_gpu(torch, fa, q, k, v, dtype, 0.1, True)
+        want = to_f64(torch, to_dev(torch, row, dtype))
+        np.testing.assert_allclose(to_f64(torch, o), np.broadcast_to(want, (1, 2, 257, 128)),
+                                   atol=TOL_O[dtype])
+
+
+def test_outputs_fully_written_and_guards_intact(torch_dev, fa):
+    torch = torch_dev
+    dtype = "f16"
+    B, H, Sq, Sk, D = 1, 3, 190, 70, 64
+    q = to_dev(torch, fi.tensor_bits(25, "q", (B, H, Sq, D), dtype), dtype)
+    k = to_dev(torch, fi.tensor_bits(25, "k", (B, H, Sk, D), dtype), dtype)
+    v = to_dev(torch, fi.tensor_bits(25, "v", (B, H, Sk, D), dtype), dtype)
+    n_o = B * H * Sq * D
+    n_l = B * H * Sq
+    guard = 4096
+    ob = torch.full((guard + n_o + guard,), float("nan"), dtype=torch.float16, device="cuda")
+    lb = torch.full((guard + n_l + guard,), float("nan"), dtype=torch.float32, device="cuda")
+    ob[:guard] = 7.0
+    ob[-guard:] = 7.0
+    lb[:guard] = 7.0
+    lb[-guard:] = 7.0
+    o = ob[guard:guard + n_o].view(B, H, Sq, D)
+    lse = lb[guard:guard + n_l].view(B, H, Sq)
+    for causal in (False, True):
+        fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+        assert bool((ob[:guard] == 7).all()) and bool((ob[-guard:] == 7).all())
+        assert bool((lb[:guard] == 7).all()) and bool((lb[-guard:] == 7).all())
+
+
+def test_deterministic(torch_dev, fa):
+    torch = torch_dev
+    w = fi.WORKLOADS["causal_b2h8_s1024_d64_f16"]
+    q, k, v = (to_dev(torch, x, w.dtype) for x in fi.make_inputs(w))
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    o2, l2 = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def test_side_stream(torch_dev, fa, oracle_mod):
+    torch = torch_dev
+    dtype = "bf16"
+    q = fi.tensor_bits(26, "q", (1, 2, 256, 128), dtype)
+    k = fi.tensor_bits(26, "k", (1, 2, 256, 128), dtype)
+    v = fi.tensor_bits(26, "v", (1, 2, 256, 128), dtype)
+    qd, kd, vd = (to_dev(torch, x, dtype) for x in (q, k, v))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = fa.fwd(qd, kd, vd, causal=False)
+    s.synchronize()
+    o_ref, l_ref = oracle_mod.attention(q, k, v, dtype, 1 / math.sqrt(128), False, threads=THREADS)
+    check(to_f64(torch, o), lse.double().cpu().numpy(), o_ref, l_ref, dtype, "side stream")
+
+
+def test_device_errors_are_host_errors(torch_dev, fa):
+    torch = torch_dev
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16, device="cuda")
+    with pytest.raises(fa.FaError):
+        fa.fwd(q, q, q, out=q)  # output aliases the input
+    with pytest.raises(fa.FaError):
+        fa.fwd(torch.zeros(1, 1, 8, 96, dtype=torch.float16, device="cuda"),
+               torch.zeros(1, 1, 8, 96, dtype=torch.float16, device="cuda"),
+               torch.zeros(1, 1, 8, 96, dtype=torch.float16, device="cuda"))
