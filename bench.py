@@ -106,7 +106,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the attention path shards over (batch, head) with no exchange; see DESIGN.md)",
+              "(the attention path shards over (batch, head) with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 

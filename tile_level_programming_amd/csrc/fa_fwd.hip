@@ -9,28 +9,44 @@
 // keys of each head are streamed in order (comrad404.com, section "Как
 // устроен туториал", FlashAttention paragraph).
 //
-// CDNA4 mapping (one work-group = one (batch, head, block of BM queries)):
+// CDNA4 mapping.  One work-group of four waves owns (batch, head, 128
+// queries); each wave owns 32 queries.  Two work-groups share a CU, so every
+// SIMD runs two independent waves and the matrix core of one overlaps the
+// vector (softmax) work of the other; registers stay within 256 per wave.
 //
-//  * Each wave owns 32 queries.  Scores are formed transposed, S^T = K Q^T,
-//    with v_mfma_f32_32x32x16_{f16,bf16}: K (from LDS) is the A operand and
-//    the wave's Q fragment (kept in VGPRs for the whole loop) is the B
-//    operand.  In the 32x32 accumulator layout a lane holds one column (one
-//    query) and 16 rows (keys), so each lane owns a query: the row maximum and
-//    sum are in-lane, plus one exchange with the lane 32 away for the max.
-//  * O is accumulated transposed as well, O^T = V^T P^T: the exponentiated
-//    scores, packed to 16 bits in registers, are directly the B operand (the
-//    lane layout of a B operand equals the accumulator's column ownership),
-//    and V^T comes from LDS.  The order in which a product's K slots visit the
-//    keys is free; the V^T tile is stored with the matching key permutation so
-//    that each lane's A fragment is one 16-byte LDS read.
-//  * The rescale factor alpha is per query, i.e. per lane: rescaling O is a
-//    plain per-lane multiply.
-//  * exp is exp2 with scale*log2(e) folded into one FMA per score.
-//  * K and V tiles of BN keys are double-buffered in LDS; the global loads of
-//    tile j+1 (128-bit, coalesced) are in flight while tile j is computed.
-//  * Causal: key tiles past the block's last query are never loaded; a wave
-//    skips the products of tiles that lie wholly above its queries; only tiles
-//    that cross the diagonal (or the end of the keys) are masked.
+//  * Scores are formed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_{f16,bf16}: K (from LDS) is the A operand and the
+//    wave's Q fragments (kept in VGPRs for the whole loop) are the B operand.
+//    In the 32x32 accumulator layout a lane holds one column (one query) and
+//    16 rows (keys), so each lane owns a query: row maximum and sum are
+//    in-lane, plus one exchange with the lane 32 away for the maximum.
+//  * O is accumulated transposed, O^T = V^T P^T: the exponentiated scores,
+//    packed to 16 bits in registers, are directly the B operand (a B
+//    operand's lane layout equals the accumulator's column ownership).  The
+//    V^T fragment is read from the V tile, kept in LDS in its natural
+//    [key][d] layout, with ds_read_b64_tr_b16 (a transposing read: in each
+//    16-lane group, lane i receives element i%4 of the 8-byte rows that lanes
+//    i/4, i/4+4, i/4+8, i/4+12 point at).  The key order of a product's K
+//    slots is free; the read addresses follow the order in which the
+//    accumulator layout holds P.
+//  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 with
+//    LDS destination: lane l of an instruction fills bytes 16l..16l+15 of a
+//    1 KB block), double-buffered, one tile ahead.  Each lane picks which
+//    16-byte chunk of the tile it fetches, which places the tile in LDS
+//    XOR-swizzled: K rows so that 16-byte fragment reads of 8 consecutive
+//    rows hit distinct banks, V rows so that the transposing reads of 4
+//    consecutive rows hit distinct banks.  The buffer's range ends at the last
+//    key, so rows past the end of the keys arrive as zeros.
+//  * Online softmax with exp2 and scale*log2(e) folded into one FMA per
+//    score.  Rescaling is lazy: a wave moves its reference maxima (and
+//    rescales O and the sums) only when some row's maximum has grown by more
+//    than 2^8 in exp2 units; otherwise the exponentials are taken against the
+//    old reference and stay below 2^8, which 16-bit P holds at full relative
+//    precision.  The reference cancels in O and is carried into lse.
+//  * Tiles that need no mask run a branch-free path; tiles that cross the
+//    causal diagonal or the end of the keys take the masked path; causal tiles
+//    wholly above a wave's queries are skipped by that wave and never loaded
+//    past the work-group's last query.
 //  * Work-group ids are remapped so that the blocks of one head land on the
 //    same XCD (each XCD has its own L2, and blocks of one head share K and V);
 //    causal heads hand out their longest blocks first.
@@ -50,8 +66,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleLog2 = 8.0f;            // lazy-rescale threshold, exp2 units
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
+constexpr int kWaves = 4;                       // waves per work-group
+constexpr int kBM = 32 * kWaves;                // queries per work-group
 
 struct Params {
   const uint16_t* q;
@@ -92,15 +114,25 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   }
 }
 
+// acc + (sum of the two fp16 values packed in w), accumulated in f32.
+__device__ __forceinline__ float add_pair_f16(uint32_t w, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+}
+
 __device__ __forceinline__ float xchg32(float x) {
   // value held by the lane 32 away (the other half of the wave)
   return __shfl_xor(x, 32, 64);
 }
 
-// Key position inside the LDS V^T row: swap bits 2 and 3 of the key index, so
-// that the 8 keys one lane feeds to one P.V product slot range are adjacent.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+__device__ __forceinline__ u32x4 lds_read_b128(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
 }
 
 // Work-group id -> logical block id.  Hardware hands consecutive ids to the
@@ -113,43 +145,86 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   return base + local;
 }
 
-template <int D, bool BF16, bool CAUSAL, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
-  constexpr int NT = NW * 64;        // threads per work-group
-  constexpr int BM = NW * 32;        // queries per work-group
-  constexpr int KS = D + 8;          // LDS row stride of the K tile (halves), padded
-  constexpr int VS = BN + 8;         // LDS row stride of the V^T tile (halves), padded
-  constexpr int STAGE = BN * KS + D * VS;
-  constexpr int CH = D / 8;          // 16-byte chunks per row
-  constexpr int NCH = BN * CH / NT;  // chunks per thread per tile and tensor
-  constexpr int KB = BN / 32;        // 32-key blocks per tile
-  constexpr int NU = BN / 16;        // 16-key slices per tile (P.V product steps)
-  constexpr int DK = D / 16;         // k-steps of the score product
-  constexpr int DB = D / 32;         // 32-wide d blocks of the output
-  static_assert(BN % 32 == 0 && (BN * CH) % NT == 0, "tile shape");
+// Stream `nld` 1 KB blocks of K and of V into LDS.  Lane l of block i fills
+// bytes 16l..16l+15 of the block at dst + i*stride (K) and dst + tile + i*stride
+// (V), reading the bytes at offk[i] / offv[i] of the tensors' rows from key k0
+// on; the buffer range ends at key Sk, so rows past it arrive as zeros.
+template <int NLD>
+__device__ __forceinline__ void load_tile_to_lds(const uint16_t* kg, const uint16_t* vg, int k0, int Sk, int rowb,
+                                                 char* dst, int tile, int stride, const int* offk,
+                                                 const int* offv) {
+  const uint32_t bytes = (uint32_t)(Sk - k0) * (uint32_t)rowb;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)kg + (size_t)k0 * rowb), (short)0, bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)vg + (size_t)k0 * rowb), (short)0, bytes, kBufferWord3);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + i * stride), 16, offk[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + tile + i * stride), 16, offv[i], 0, 0, 0);
+  }
+}
 
-  __shared__ u32x4 lds_raw[(2 * STAGE * 2 + 15) / 16];
-  uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
+struct NoMask { static constexpr bool value = false; };
+struct Mask { static constexpr bool value = true; };
+
+template <int D, bool BF16, bool CAUSAL, int BN>
+__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
+  constexpr int CH = D / 8;                       // 16-byte chunks per row
+  constexpr int ROWB = 2 * D;                     // bytes per row
+  constexpr int TILE = BN * ROWB;                 // bytes of one K or V tile
+  constexpr int STAGE = 2 * TILE;                 // K tile then V tile
+  constexpr int NLD = TILE / 16 / (64 * kWaves);  // load instructions per wave per tensor
+  constexpr int KB = BN / 32;                     // 32-key blocks per tile
+  constexpr int NU = BN / 16;                     // 16-key slices per tile (P.V product steps)
+  constexpr int DK = D / 16;                      // k-steps of the score product
+  constexpr int DB = D / 32;                      // 32-wide d blocks of the output
+  static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over the waves");
+
+  // Two stages as two separate arrays: the compiler can then tell that the
+  // loads streaming into one stage never alias the reads from the other.
+  __shared__ u32x4 stage0[STAGE / 16];
+  __shared__ u32x4 stage1[STAGE / 16];
+  char* const buf0 = reinterpret_cast<char*>(stage0);
+  char* const buf1 = reinterpret_cast<char*>(stage1);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int n = lane & 31;   // query column owned by this lane
-  const int h = lane >> 5;   // which half of the wave
+  const int n = lane & 31;  // query column owned by this lane
+  const int h = lane >> 5;  // which half of the wave
 
   const int t = xcd_remap(blockIdx.x, p.n_wg);
   const int bh = t / p.n_qblk;
-  int qb = t - bh * p.n_qblk;
-  if (CAUSAL) qb = p.n_qblk - 1 - qb;  // longest blocks first
-  const int q0 = qb * BM;
-  const int qw0 = q0 + wave * 32;     // first query of this wave
-  const int qi = qw0 + n;             // query of this lane
+  int qblk = t - bh * p.n_qblk;
+  if (CAUSAL) qblk = p.n_qblk - 1 - qblk;  // longest blocks first
+  const int q0 = qblk * kBM;
+  const int qw0 = q0 + wave * 32;  // first query of this wave
+  const int qi = qw0 + n;          // query of this lane
 
   const uint16_t* qg = p.q + (size_t)bh * p.Sq * D;
   const uint16_t* kg = p.k + (size_t)bh * p.Sk * D;
   const uint16_t* vg = p.v + (size_t)bh * p.Sk * D;
 
-  // ---- Q fragment: B operand of S^T = K Q^T, lane holds q[qi][16*ks + 8*h .. +8]
+  const int kend = CAUSAL ? min(p.Sk, q0 + kBM) : p.Sk;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  // ---- tile loads: each lane fetches the global chunk that belongs at its LDS slot
+  int offk[NLD], offv[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int slot = (i * kWaves + wave) * 64 + lane;  // 16-byte slot within the tile
+    const int r = slot / CH, pc = slot % CH;
+    offk[i] = r * ROWB + ((pc ^ (r & 7)) << 4);
+    offv[i] = r * ROWB + ((pc ^ ((r & 3) << 1)) << 4);
+  }
+  auto issue_tile = [&](int tile, char* stage) {
+    load_tile_to_lds<NLD>(kg, vg, tile * BN, p.Sk, ROWB, stage + wave * 1024, TILE, kWaves * 1024, offk, offv);
+  };
+
+  issue_tile(0, buf0);
+
+  // ---- Q fragments: B operands of S^T = K Q^T; lane holds q[qi][16*ks + 8*h .. +8]
   u32x4 qf[DK];
 #pragma unroll
   for (int ks = 0; ks < DK; ++ks) {
@@ -159,43 +234,23 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
     qf[ks] = x;
   }
 
-  const int kend = CAUSAL ? min(p.Sk, q0 + BM) : p.Sk;
-  const int ntiles = (kend + BN - 1) / BN;
-
-  // ---- global -> register staging of one K and V tile
-  u32x4 kr[NCH], vr[NCH];
-  auto gload = [&](int k0) {
+  // ---- per-lane fragment read offsets (bytes within a stage)
+  // K (A operand of S^T): row 32*kb + n, logical chunk 2*ks + h, swizzled by row & 7.
+  int koff[DK];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int cidx = tid + i * NT;
-      const int row = cidx / CH, col = cidx % CH;
-      const int key = k0 + row;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (key < p.Sk) {
-        a = *reinterpret_cast<const u32x4*>(kg + (size_t)key * D + col * 8);
-        b = *reinterpret_cast<const u32x4*>(vg + (size_t)key * D + col * 8);
-      }
-      kr[i] = a;
-      vr[i] = b;
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint16_t* ks_ = lds + buf * STAGE;
-    uint16_t* vt_ = ks_ + BN * KS;
+  for (int ks = 0; ks < DK; ++ks) koff[ks] = n * ROWB + (((2 * ks + h) ^ (n & 7)) << 4);
+  // V (A operand of O^T through the transposing read): in 16-lane group g
+  // (lane = 16g + s) source lane s points at row 4*(g/2) + s/4 (+ 16u + 8*half)
+  // and element 32*db + 16*(g%2) + 4*(s%4); the lane then receives
+  // d = 32*db + lane%32 for keys 16u + 8*half + 4*h + (0..3).
+  const int g = lane >> 4, s = lane & 15;
+  const int vrow = 4 * (g >> 1) + (s >> 2);
+  int voff[DB];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int cidx = tid + i * NT;
-      const int row = cidx / CH, col = cidx % CH;
-      *reinterpret_cast<u32x4*>(ks_ + row * KS + col * 8) = kr[i];
-      const int pos = vt_pos(row);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = vr[i][e];
-        vt_[(col * 8 + 2 * e) * VS + pos] = (uint16_t)(w & 0xFFFFu);
-        vt_[(col * 8 + 2 * e + 1) * VS + pos] = (uint16_t)(w >> 16);
-      }
-    }
-  };
+  for (int db = 0; db < DB; ++db) {
+    const int chunk = 4 * db + 2 * (g & 1) + ((s & 3) >> 1);
+    voff[db] = vrow * ROWB + ((chunk ^ ((vrow & 3) << 1)) << 4) + ((s & 1) << 3);
+  }
 
   // ---- running state of this lane's query
   f32x16 oacc[DB];
@@ -203,133 +258,155 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY;  // running max of the raw (unscaled) scores
+  float m_ref = -INFINITY;  // reference maximum of the raw (unscaled) scores
   float l_run = 0.f;        // this half's share of the running normaliser
   const float c = p.c;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  auto compute = [&](const char* st, int k0, auto masked_tag) {
+    constexpr bool MASK = decltype(masked_tag)::value;
+    const char* kt = st;
+    const char* vt = st + TILE;
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * BN;
-    if (j + 1 < ntiles) gload(k0 + BN);
+    // S^T = K Q^T: sacc[kb][r] = score(query qi, key k0 + 32kb + 8(r/4) + 4h + r%4)
+    f32x16 sacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks)
+        sacc[kb] = mfma_32x32x16<BF16>(lds_read_b128(kt, koff[ks] + kb * 32 * ROWB), qf[ks], sacc[kb]);
+    }
 
-    const bool active = !CAUSAL || k0 <= qw0 + 31;  // some key of the tile is visible to the wave
-    if (active && qw0 < p.Sq) {
-      const uint16_t* ks_ = lds + (j & 1) * STAGE;
-      const uint16_t* vt_ = ks_ + BN * KS;
-
-      // S^T = K Q^T for the tile: s[kb][r] = score(query qi, key k0 + 32kb + 8(r/4) + 4h + r%4)
-      f32x16 s[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(ks_ + (kb * 32 + n) * KS + ks * 16 + h * 8);
-          s[kb] = mfma_32x32x16<BF16>(a, qf[ks], s[kb]);
-        }
-      }
-
-      const bool masked = (k0 + BN > p.Sk) || (CAUSAL && k0 + BN - 1 > qw0);
-      if (masked) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool hide = key >= p.Sk || (CAUSAL && key > qi);
-            if (hide) s[kb][r] = -INFINITY;
-          }
-      }
-
-      // online softmax: new running max, rescale factor, probabilities
-      float mx = s[0][0];
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, xchg32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f((m_run - m_new) * c);
-      const float mc = m_new * c;
-      m_run = m_new;
-
-      float psum = 0.f;
-      u32x4 pf[NU];
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        float pv[8];
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) {
-          const float sv = s[u >> 1][8 * (u & 1) + t8];
-          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -mc));
-          if (masked && sv == -INFINITY) pe = 0.f;
-          pv[t8] = pe;
-          psum += pe;
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= p.Sk || (CAUSAL && key > qi)) sacc[kb][r] = -INFINITY;
         }
-        pf[u][0] = pack2<BF16>(pv[0], pv[1]);
-        pf[u][1] = pack2<BF16>(pv[2], pv[3]);
-        pf[u][2] = pack2<BF16>(pv[4], pv[5]);
-        pf[u][3] = pack2<BF16>(pv[6], pv[7]);
-      }
-      l_run = alpha * l_run + psum;
+    }
+
+    // tile row max (both halves of the wave)
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, xchg32(mx));
+
+    // lazy rescale: move the reference only when some row's max grew past the threshold
+    const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c > kRescaleLog2);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int u = 0; u < NU; ++u)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(vt_ + (db * 32 + n) * VS + u * 16 + h * 8);
-          oacc[db] = mfma_32x32x16<BF16>(a, pf[u], oacc[db]);
-        }
     }
+    const float mc = m_ref * c;
 
-    if (j + 1 < ntiles) sstore((j + 1) & 1);
+    // P = exp2(s*c - m*c), packed to 16 bits; running sum
+    u32x4 pf[NU];
+    float psum = l_run;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      float pv[8];
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) {
+        const float sv = sacc[u >> 1][8 * (u & 1) + t8];
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -mc));
+        if constexpr (MASK) pe = (sv == -INFINITY) ? 0.f : pe;  // also covers scale == 0
+        pv[t8] = pe;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[u][e] = pack2<BF16>(pv[2 * e], pv[2 * e + 1]);
+        // fp16 rounds P to within 2^-12, so summing the rounded values keeps the
+        // normaliser (and lse) accurate; bf16 rounding (2^-9) would not, so bf16
+        // sums the fp32 values.
+        if constexpr (BF16)
+          psum += pv[2 * e] + pv[2 * e + 1];
+        else
+          psum = add_pair_f16(pf[u][e], psum);
+      }
+    }
+    l_run = psum;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char* vp = vt + voff[db] + 16 * u * ROWB;
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi = lds_read_tr16(vp + 8 * ROWB);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = mfma_32x32x16<BF16>(a, pf[u], oacc[db]);
+      }
+  };
+
+  auto step = [&](int j, const char* cur, char* nxt) {
+    // tile j resident for every wave; every wave done with tile j-1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (j + 1 < ntiles) issue_tile(j + 1, nxt);
+
+    const int k0 = j * BN;
+    const bool skip = CAUSAL && k0 > qw0 + 31;  // every key of the tile is above this wave's queries
+    const bool need_mask = (k0 + BN > p.Sk) || (CAUSAL && k0 + BN - 1 > qw0);
+    if (!skip && qw0 < p.Sq) {
+      if (need_mask)
+        compute(cur, k0, Mask{});
+      else
+        compute(cur, k0, NoMask{});
+    }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, buf0, buf1);
+    if (j + 1 < ntiles) step(j + 1, buf1, buf0);
   }
 
   // ---- epilogue: normalise, round, store O rows and lse
-  if (qi < p.Sq) {
+  if (qw0 < p.Sq) {
     const float l = l_run + xchg32(l_run);
-    const float inv = 1.f / l;
-    uint16_t* og = p.o + ((size_t)bh * p.Sq + qi) * D;
+    if (qi < p.Sq) {
+      const float inv = 1.f / l;
+      uint16_t* og = p.o + ((size_t)bh * p.Sq + qi) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * h;
-        u32x2 w;
-        w[0] = pack2<BF16>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-        w[1] = pack2<BF16>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(og + d0) = w;
-      }
-    if (h == 0) p.lse[(size_t)bh * p.Sq + qi] = (m_run * c + __log2f(l)) * kLn2;
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = db * 32 + 8 * gq + 4 * h;
+          u32x2 w;
+          w[0] = pack2<BF16>(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv);
+          w[1] = pack2<BF16>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
+          *reinterpret_cast<u32x2*>(og + d0) = w;
+        }
+      if (h == 0) p.lse[(size_t)bh * p.Sq + qi] = (m_ref * c + __log2f(l)) * kLn2;
+    }
   }
 }
 
+// Keys per tile for each (head dim, dtype, mask).
 template <int D, bool BF16, bool CAUSAL>
 struct Cfg {
-  static constexpr int NW = 4;
-  static constexpr int BN = 64;
+  static constexpr int BN = D == 64 ? 64 : 32;
 };
 
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream) {
   using C = Cfg<D, BF16, CAUSAL>;
-  constexpr int BM = C::NW * 32;
   Params p = base;
-  p.n_qblk = (int)((Sq + BM - 1) / BM);
+  p.n_qblk = (int)((Sq + kBM - 1) / kBM);
   p.n_wg = (int)(BH * p.n_qblk);
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::NW, C::BN>),
-                         dim3(p.n_wg), dim3(C::NW * 64), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN>),
+                         dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -353,7 +430,7 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
   if (Sq >= lim / D || Sk >= lim / D) return FA_ERR_INVALID_ARG;
   if (B >= lim / H) return FA_ERR_INVALID_ARG;
   const int64_t BH = B * H;
-  const int64_t minBM = 128;
+  const int64_t minBM = kBM;  // queries per work-group
   if (BH >= lim / ((Sq + minBM - 1) / minBM)) return FA_ERR_INVALID_ARG;
   // element counts in int64: BH < 2^31 and S*D < 2^31 keep these below 2^62
   const size_t qo_bytes = (size_t)(BH * Sq * D) * 2, kv_bytes = (size_t)(BH * Sk * D) * 2;
