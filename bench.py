@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--workload", default=fi.HEADLINE, choices=list(fi.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB 10 times (calibrates the "
+                         "HBM byte counters against a kernel of known traffic) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -113,6 +116,16 @@ def main():
     import torch
 
     from tile_level_programming_amd import fa
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 10 copies of {n} bytes (read {n} B + write {n} B each)")
+        return
 
     w = fi.WORKLOADS[args.workload]
     log(f"[bench] workload {w.name}: generating seeded inputs")
@@ -138,21 +151,34 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # HIP events on the launch stream: one pair around the whole timed region
+    # (throughput) and one pair around every launch (mean kernel duration for
+    # the roofline; back-to-back launches, so the two agree to within the
+    # event overhead)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
+    for e0, e1 in ev:
+        e0.record(stream)
         step()
+        e1.record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms = ms_total / args.steps
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms_kernel = float(np.mean(launch_ms))
     flop = w.flops()
     tflops = flop / (ms * 1e-3) / 1e12
-    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s (wall {wall:.3f} s)")
+    tflops_kernel = flop / (ms_kernel * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s; per launch "
+        f"mean {ms_kernel:.4f} ms (min {min(launch_ms):.4f}, max {max(launch_ms):.4f}), "
+        f"{tflops_kernel:.1f} TFLOP/s (wall {wall:.3f} s)")
 
     # sampled parity of the timed output
     import oracle
@@ -193,9 +219,10 @@ def main():
                    "causal": w.causal, "scale": w.scale, "algorithmic_flop": flop,
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS_F16, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_F16,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS_F16, 4),
-                     "traffic": traffic},
+        "roofline": {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": PEAK_TFLOPS_F16,
+                     "unit": "TFLOP/s", "frac": round(tflops_kernel / PEAK_TFLOPS_F16, 4),
+                     "traffic": traffic, "kernel_ms": round(ms_kernel, 5),
+                     "algorithmic_flop_per_launch": flop},
         "cpu_baseline": cpu,
         "parity_sample": {"rows": int(rows.size), "max_abs_err_o": err_o, "max_rel_err_lse": err_l,
                           "ok": parity_ok},
