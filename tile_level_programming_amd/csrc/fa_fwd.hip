@@ -11,15 +11,15 @@
 //
 // CDNA4 mapping.  One work-group of four waves owns (batch, head, 128
 // queries); each wave owns 32 queries.  Two work-groups share a CU, so every
-// SIMD runs two independent waves and the matrix core of one overlaps the
-// vector (softmax) work of the other; registers stay within 256 per wave.
+// SIMD runs two independent waves; registers stay within 256 per wave.
 //
 //  * Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{f16,bf16}: K (from LDS) is the A operand and the
 //    wave's Q fragments (kept in VGPRs for the whole loop) are the B operand.
 //    In the 32x32 accumulator layout a lane holds one column (one query) and
 //    16 rows (keys), so each lane owns a query: row maximum and sum are
-//    in-lane, plus one exchange with the lane 32 away for the maximum.
+//    in-lane, plus one swap with the other half of the wave
+//    (v_permlane32_swap).
 //  * O is accumulated transposed, O^T = V^T P^T: the exponentiated scores,
 //    packed to 16 bits in registers, are directly the B operand (a B
 //    operand's lane layout equals the accumulator's column ownership).  The
@@ -29,14 +29,20 @@
 //    i/4, i/4+4, i/4+8, i/4+12 point at).  The key order of a product's K
 //    slots is free; the read addresses follow the order in which the
 //    accumulator layout holds P.
+//  * Software pipeline across key tiles: while the vector unit exponentiates
+//    tile j, the matrix unit computes the scores of tile j+1 and the P.V
+//    product of tile j, with the instructions interleaved so one wave keeps
+//    both units busy.  K therefore runs one tile ahead of V in LDS: at tile j
+//    the K tile j+1 and the V tile j are resident while K j+2 and V j+1
+//    stream in.
 //  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 with
 //    LDS destination: lane l of an instruction fills bytes 16l..16l+15 of a
-//    1 KB block), double-buffered, one tile ahead.  Each lane picks which
-//    16-byte chunk of the tile it fetches, which places the tile in LDS
-//    XOR-swizzled: K rows so that 16-byte fragment reads of 8 consecutive
-//    rows hit distinct banks, V rows so that the transposing reads of 4
-//    consecutive rows hit distinct banks.  The buffer's range ends at the last
-//    key, so rows past the end of the keys arrive as zeros.
+//    1 KB block).  Each lane picks which 16-byte chunk of the tile it fetches,
+//    which places the tile in LDS XOR-swizzled for the 64-bank LDS: K rows so
+//    that the 16-byte fragment reads of 16 consecutive rows hit distinct
+//    banks, V rows so that the transposing reads of 4 consecutive rows hit
+//    distinct banks.  The buffer's range ends at the last key, so rows past
+//    the end of the keys arrive as zeros.
 //  * Online softmax with exp2 and scale*log2(e) folded into one FMA per
 //    score.  Rescaling is lazy: a wave moves its reference maxima (and
 //    rescales O and the sums) only when some row's maximum has grown by more
@@ -74,6 +80,11 @@ constexpr float kRescaleLog2 = 8.0f;            // lazy-rescale threshold, exp2 
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr int kWaves = 4;                       // waves per work-group
 constexpr int kBM = 32 * kWaves;                // queries per work-group
+
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 struct Params {
   const uint16_t* q;
@@ -120,9 +131,17 @@ __device__ __forceinline__ float add_pair_f16(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
 }
 
-__device__ __forceinline__ float xchg32(float x) {
-  // value held by the lane 32 away (the other half of the wave)
-  return __shfl_xor(x, 32, 64);
+// v_permlane32_swap exchanges the two 32-lane halves of a wave: afterwards
+// the pair holds, in every lane, the values of lane l%32 and lane l%32+32.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 __device__ __forceinline__ u32x4 lds_read_b128(const char* base, int off) {
@@ -145,51 +164,69 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   return base + local;
 }
 
-// Stream `nld` 1 KB blocks of K and of V into LDS.  Lane l of block i fills
-// bytes 16l..16l+15 of the block at dst + i*stride (K) and dst + tile + i*stride
-// (V), reading the bytes at offk[i] / offv[i] of the tensors' rows from key k0
-// on; the buffer range ends at key Sk, so rows past it arrive as zeros.
-template <int NLD>
-__device__ __forceinline__ void load_tile_to_lds(const uint16_t* kg, const uint16_t* vg, int k0, int Sk, int rowb,
-                                                 char* dst, int tile, int stride, const int* offk,
-                                                 const int* offv) {
-  const uint32_t bytes = (uint32_t)(Sk - k0) * (uint32_t)rowb;
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)kg + (size_t)k0 * rowb), (short)0, bytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)vg + (size_t)k0 * rowb), (short)0, bytes, kBufferWord3);
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + i * stride), 16, offk[i], 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + tile + i * stride), 16, offv[i], 0, 0, 0);
-  }
+// LDS swizzles, in 16-byte chunks.  The LDS has 64 four-byte banks (256
+// bytes); a 16-byte read by a wave is served 16 lanes at a time and a 8-byte
+// transposing read 32 lanes at a time.
+//  K: the score product's A fragment reads logical chunk c of 16 consecutive
+//     rows in one pass; physical chunk c ^ ksw(row) puts them in 16 distinct
+//     bank groups (D=64: two rows share a 256-byte bank line).
+//  V: the transposing read covers 4 consecutive rows x 4 consecutive chunks
+//     per pass; physical chunk c ^ vsw(row) spreads them over 16 groups.
+template <int D>
+__device__ __forceinline__ int ksw(int r) {
+  return D == 64 ? ((r >> 1) & 7) : (r & 15);
+}
+template <int D>
+__device__ __forceinline__ int vsw(int r) {
+  return D == 64 ? ((r & 3) << 1) : ((r & 3) << 2);
 }
 
-struct NoMask { static constexpr bool value = false; };
-struct Mask { static constexpr bool value = true; };
+// Stream NLD 1 KB blocks of one tensor's rows k0.. into LDS.  Lane l of
+// block i fills bytes 16l..16l+15 of the block at dst + i*stride, reading the
+// bytes at off[i] of the rows from key k0 on; the buffer range ends at key
+// Sk, so rows past it arrive as zeros.
+template <int NLD>
+__device__ __forceinline__ void load_rows_to_lds(const uint16_t* g, int k0, int Sk, int rowb, char* dst,
+                                                 int stride, const int* off) {
+  const uint32_t bytes = (uint32_t)(Sk - k0) * (uint32_t)rowb;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)g + (size_t)k0 * rowb), (short)0, bytes, kBufferWord3);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * stride), 16, off[i], 0, 0, 0);
+}
+
+template <bool B>
+struct Flag { static constexpr bool value = B; };
 
 template <int D, bool BF16, bool CAUSAL, int BN>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                     // bytes per row
   constexpr int TILE = BN * ROWB;                 // bytes of one K or V tile
-  constexpr int STAGE = 2 * TILE;                 // K tile then V tile
-  constexpr int NLD = TILE / 16 / (64 * kWaves);  // load instructions per wave per tensor
+  constexpr int NLD = TILE / 16 / (64 * kWaves);  // load instructions per wave per tile
   constexpr int KB = BN / 32;                     // 32-key blocks per tile
   constexpr int NU = BN / 16;                     // 16-key slices per tile (P.V product steps)
   constexpr int DK = D / 16;                      // k-steps of the score product
   constexpr int DB = D / 32;                      // 32-wide d blocks of the output
+  constexpr int NS = KB * DK;                     // score products per tile
+  constexpr int NSA = NS / 2;                     // of which issued ahead of the row maximum
   static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over the waves");
+  static_assert(DK >= NSA, "the early score products must share one 32-key block");
 
-  // Two stages as two separate arrays: the compiler can then tell that the
-  // loads streaming into one stage never alias the reads from the other.
-  __shared__ u32x4 stage0[STAGE / 16];
-  __shared__ u32x4 stage1[STAGE / 16];
-  char* const buf0 = reinterpret_cast<char*>(stage0);
-  char* const buf1 = reinterpret_cast<char*>(stage1);
+  // K and V stages as four separate arrays: the compiler can then tell that
+  // the loads streaming into one array never alias the reads from another.
+  __shared__ u32x4 kst0[TILE / 16];
+  __shared__ u32x4 kst1[TILE / 16];
+  __shared__ u32x4 vst0[TILE / 16];
+  __shared__ u32x4 vst1[TILE / 16];
+  char* const kb0 = reinterpret_cast<char*>(kst0);
+  char* const kb1 = reinterpret_cast<char*>(kst1);
+  char* const vb0 = reinterpret_cast<char*>(vst0);
+  char* const vb1 = reinterpret_cast<char*>(vst1);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave branches scalar
   const int lane = tid & 63;
   const int n = lane & 31;  // query column owned by this lane
   const int h = lane >> 5;  // which half of the wave
@@ -208,6 +245,18 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
 
   const int kend = CAUSAL ? min(p.Sk, q0 + kBM) : p.Sk;
   const int ntiles = (kend + BN - 1) / BN;
+  // tiles this wave computes: all of the work-group's, less (causal) those
+  // wholly above its last query; none for waves past the last query
+  int nt_w = CAUSAL ? min(ntiles, (qw0 + 31) / BN + 1) : ntiles;
+  if (qw0 >= p.Sq) nt_w = 0;
+  // the first tile that needs a mask: the one holding the end of the keys
+  // (when Sk is not a multiple of BN) or, causal, the first that reaches past
+  // this wave's first query
+  int j_mask = p.Sk / BN;
+  if (CAUSAL) j_mask = min(j_mask, (qw0 + 1) / BN);
+  // tiles 0 .. j_fast-1 need no mask and have a successor: the branch-free
+  // loop runs them in pairs
+  const int j_fast = max(0, min(nt_w - 1, j_mask)) & ~1;
 
   // ---- tile loads: each lane fetches the global chunk that belongs at its LDS slot
   int offk[NLD], offv[NLD];
@@ -215,14 +264,19 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int i = 0; i < NLD; ++i) {
     const int slot = (i * kWaves + wave) * 64 + lane;  // 16-byte slot within the tile
     const int r = slot / CH, pc = slot % CH;
-    offk[i] = r * ROWB + ((pc ^ (r & 7)) << 4);
-    offv[i] = r * ROWB + ((pc ^ ((r & 3) << 1)) << 4);
+    offk[i] = r * ROWB + ((pc ^ ksw<D>(r)) << 4);
+    offv[i] = r * ROWB + ((pc ^ vsw<D>(r)) << 4);
   }
-  auto issue_tile = [&](int tile, char* stage) {
-    load_tile_to_lds<NLD>(kg, vg, tile * BN, p.Sk, ROWB, stage + wave * 1024, TILE, kWaves * 1024, offk, offv);
+  auto issue_k = [&](int tile, char* buf) {
+    load_rows_to_lds<NLD>(kg, tile * BN, p.Sk, ROWB, buf + wave * 1024, kWaves * 1024, offk);
+  };
+  auto issue_v = [&](int tile, char* buf) {
+    load_rows_to_lds<NLD>(vg, tile * BN, p.Sk, ROWB, buf + wave * 1024, kWaves * 1024, offv);
   };
 
-  issue_tile(0, buf0);
+  issue_k(0, kb0);
+  issue_v(0, vb0);
+  if (ntiles > 1) issue_k(1, kb1);
 
   // ---- Q fragments: B operands of S^T = K Q^T; lane holds q[qi][16*ks + 8*h .. +8]
   u32x4 qf[DK];
@@ -234,11 +288,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     qf[ks] = x;
   }
 
-  // ---- per-lane fragment read offsets (bytes within a stage)
-  // K (A operand of S^T): row 32*kb + n, logical chunk 2*ks + h, swizzled by row & 7.
+  // ---- per-lane fragment read offsets (bytes within a tile)
+  // K (A operand of S^T): row 32*kb + n, logical chunk 2*ks + h.
   int koff[DK];
 #pragma unroll
-  for (int ks = 0; ks < DK; ++ks) koff[ks] = n * ROWB + (((2 * ks + h) ^ (n & 7)) << 4);
+  for (int ks = 0; ks < DK; ++ks) koff[ks] = n * ROWB + (((2 * ks + h) ^ ksw<D>(n)) << 4);
   // V (A operand of O^T through the transposing read): in 16-lane group g
   // (lane = 16g + s) source lane s points at row 4*(g/2) + s/4 (+ 16u + 8*half)
   // and element 32*db + 16*(g%2) + 4*(s%4); the lane then receives
@@ -249,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int chunk = 4 * db + 2 * (g & 1) + ((s & 3) >> 1);
-    voff[db] = vrow * ROWB + ((chunk ^ ((vrow & 3) << 1)) << 4) + ((s & 1) << 3);
+    voff[db] = vrow * ROWB + ((chunk ^ vsw<D>(vrow)) << 4) + ((s & 1) << 3);
   }
 
   // ---- running state of this lane's query
@@ -262,20 +316,28 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   float l_run = 0.f;        // this half's share of the running normaliser
   const float c = p.c;
 
-  auto compute = [&](const char* st, int k0, auto masked_tag) {
-    constexpr bool MASK = decltype(masked_tag)::value;
-    const char* kt = st;
-    const char* vt = st + TILE;
+  // i-th score product of a tile: S^T[32kb.., q] += K[32kb + n][16ks + 8h ..] q[..]
+  auto score_mfma = [&](f32x16* sacc, const char* kt, int i) {
+    const int kb = i / DK, ks = i % DK;
+    sacc[kb] = mfma_32x32x16<BF16>(lds_read_b128(kt, koff[ks] + kb * 32 * ROWB), qf[ks], sacc[kb]);
+  };
 
-    // S^T = K Q^T: sacc[kb][r] = score(query qi, key k0 + 32kb + 8(r/4) + 4h + r%4)
-    f32x16 sacc[KB];
+  // One key tile: softmax and P.V of tile j (scores in sacc, V tile at vt),
+  // and, when NEXT, the scores of tile j+1 into snext from the K tile at kn.
+  // sacc[kb][r] = score(query qi, key k0 + 32kb + 8(r/4) + 4h + r%4).
+  auto tile_step = [&](f32x16* sacc, f32x16* snext, const char* kn, const char* vt, int k0, auto mask_tag,
+                       auto next_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
+
+    // the first half of the next tile's score products runs under the row max
+    if constexpr (NEXT) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) snext[kb][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks)
-        sacc[kb] = mfma_32x32x16<BF16>(lds_read_b128(kt, koff[ks] + kb * 32 * ROWB), qf[ks], sacc[kb]);
+      for (int i = 0; i < NSA; ++i) score_mfma(snext, kn, i);
     }
 
     if constexpr (MASK) {
@@ -294,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, xchg32(mx));
+    mx = max_halves(mx);
 
     // lazy rescale: move the reference only when some row's max grew past the threshold
     const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c > kRescaleLog2);
@@ -348,32 +410,93 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         oacc[db] = mfma_32x32x16<BF16>(a, pf[u], oacc[db]);
       }
-  };
 
-  auto step = [&](int j, const char* cur, char* nxt) {
-    // tile j resident for every wave; every wave done with tile j-1
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 < ntiles) issue_tile(j + 1, nxt);
+    // the second half of the next tile's score products
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int i = NSA; i < NS; ++i) score_mfma(snext, kn, i);
+    }
 
-    const int k0 = j * BN;
-    const bool skip = CAUSAL && k0 > qw0 + 31;  // every key of the tile is above this wave's queries
-    const bool need_mask = (k0 + BN > p.Sk) || (CAUSAL && k0 + BN - 1 > qw0);
-    if (!skip && qw0 < p.Sq) {
-      if (need_mask)
-        compute(cur, k0, Mask{});
-      else
-        compute(cur, k0, NoMask{});
+    // Interleave: one matrix instruction, then a run of vector instructions
+    // and LDS reads, so the wave keeps the matrix unit busy while it
+    // exponentiates.
+    constexpr int NMF = NU * DB + (NEXT ? NS - NSA : 0);
+    constexpr int NVALU = NU * (8 + 8 + 4 + (BF16 ? 8 : 4));
+    constexpr int VPM = (NVALU + NMF - 1) / NMF;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, VPM, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
   };
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, buf0, buf1);
-    if (j + 1 < ntiles) step(j + 1, buf1, buf0);
+
+  // K tile j+1 and V tile j resident for every wave; every wave is done
+  // with K tile j (read for the scores last step) and V tile j-1; start the
+  // loads of K tile j+2 and V tile j+1
+  auto stage = [&](int j, char* kfree, char* vnext) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 2 < ntiles) issue_k(j + 2, kfree);
+    if (j + 1 < ntiles) issue_v(j + 1, vnext);
+  };
+  auto step_fast = [&](int j, char* kfree, const char* knext, const char* vcur, char* vnext, f32x16* sacc,
+                       f32x16* snext) {
+    stage(j, kfree, vnext);
+    tile_step(sacc, snext, knext, vcur, j * BN, Flag<false>{}, Flag<true>{});
+  };
+  // any tile: masked or not, with or without a successor; the scores of the
+  // successor land in snext and are moved to sacc
+  auto step = [&](int j, f32x16* sacc, f32x16* snext) {
+    const bool odd = j & 1;
+    stage(j, odd ? kb1 : kb0, odd ? vb0 : vb1);
+    if (j < nt_w) {
+      const char* knext = odd ? kb0 : kb1;
+      const char* vcur = odd ? vb1 : vb0;
+      const int k0 = j * BN;
+      const bool next = j + 1 < nt_w;
+      const bool need_mask = (k0 + BN > p.Sk) || (CAUSAL && k0 + BN - 1 > qw0);
+      if (need_mask) {
+        if (next)
+          tile_step(sacc, snext, knext, vcur, k0, Flag<true>{}, Flag<true>{});
+        else
+          tile_step(sacc, snext, knext, vcur, k0, Flag<true>{}, Flag<false>{});
+      } else {
+        if (next)
+          tile_step(sacc, snext, knext, vcur, k0, Flag<false>{}, Flag<true>{});
+        else
+          tile_step(sacc, snext, knext, vcur, k0, Flag<false>{}, Flag<false>{});
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sacc[kb] = snext[kb];
+    }
+  };
+
+  // scores of tile 0
+  f32x16 sa[KB], sb[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sa[kb][r] = 0.f;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (nt_w > 0) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) score_mfma(sa, kb0, i);
   }
+
+  // K tile t lives in kb[t&1], V tile t in vb[t&1]
+  int j = 0;
+  for (; j < j_fast; j += 2) {
+    step_fast(j, kb0, kb1, vb0, vb1, sa, sb);
+    step_fast(j + 1, kb1, kb0, vb1, vb0, sb, sa);
+  }
+  for (; j < ntiles; ++j) step(j, sa, sb);
 
   // ---- epilogue: normalise, round, store O rows and lse
   if (qw0 < p.Sq) {
-    const float l = l_run + xchg32(l_run);
+    const float l = sum_halves(l_run);
     if (qi < p.Sq) {
       const float inv = 1.f / l;
       uint16_t* og = p.o + ((size_t)bh * p.Sq + qi) * D;
