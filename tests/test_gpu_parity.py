@@ -138,6 +138,27 @@ def test_odd_shapes(torch_dev, fa, oracle_mod, shape, causal, dtype):
     full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(D), causal, f"{shape} {causal} {dtype}")
 
 
+# Many heads with short, ragged sequences: grids of hundreds of work-groups
+# whose query and key ends fall inside tiles.
+WIDE = [
+    # (B, H, Sq, Sk, D)
+    (2, 128, 200, 333, 64), (1, 256, 77, 77, 128), (4, 64, 300, 129, 128), (1, 256, 256, 1000, 64),
+    (1, 256, 257, 31, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", WIDE)
+def test_wide_grid_shapes(torch_dev, fa, oracle_mod, shape, causal, dtype):
+    B, H, Sq, Sk, D = shape
+    seed = 300 + Sq + 3 * Sk + D
+    q = fi.tensor_bits(seed, "q", (B, H, Sq, D), dtype)
+    k = fi.tensor_bits(seed, "k", (B, H, Sk, D), dtype)
+    v = fi.tensor_bits(seed, "v", (B, H, Sk, D), dtype)
+    full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(D), causal, f"{shape} {causal} {dtype}")
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 1.0, 3.0])
 @pytest.mark.parametrize("causal", [False, True])
 def test_scales(torch_dev, fa, oracle_mod, scale, causal):

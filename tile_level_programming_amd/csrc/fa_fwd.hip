@@ -97,6 +97,7 @@ struct Params {
   int n_wg;        // total work-groups
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 when scale < 0 (q is negated on load), else 0
+  float cs;        // scale * log2(e), by which q is multiplied on load when pre-scaling
 };
 
 template <bool BF16>
@@ -142,6 +143,15 @@ __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                                   __builtin_bit_cast(uint32_t, x), false, false);
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// max(a, b, c) as one v_max3_f32.  Written out because fmaxf would first
+// quiet each input (the kernel runs with IEEE mode on), one extra instruction
+// per input; a NaN score still reaches the output through its exponential.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 __device__ __forceinline__ u32x4 lds_read_b128(const char* base, int off) {
@@ -199,7 +209,13 @@ __device__ __forceinline__ void load_rows_to_lds(const uint16_t* g, int k0, int 
 template <bool B>
 struct Flag { static constexpr bool value = B; };
 
-template <int D, bool BF16, bool CAUSAL, int BN>
+// PRE: q is multiplied by scale*log2(e) (rounded to fp16) when it is loaded,
+// so the score products give exp2-domain logits directly, and the scores a
+// step exponentiates are kept relative to the row's reference.  A row's
+// first reference is 0 when its first maximum lies within +-kRescaleLog2 of
+// 0 (moderate logits); while every row of a wave has the reference 0,
+// P = exp2(s) needs no subtraction at all.
+template <int D, bool BF16, bool CAUSAL, int BN, bool PRE>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                     // bytes per row
@@ -212,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int NS = KB * DK;                     // score products per tile
   constexpr int NSA = NS / 2;                     // of which issued ahead of the row maximum
   static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over the waves");
+  static_assert(!(PRE && BF16), "pre-scaling rounds q to fp16");
   static_assert(DK >= NSA, "the early score products must share one 32-key block");
 
   // K and V stages as four separate arrays: the compiler can then tell that
@@ -284,7 +301,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int ks = 0; ks < DK; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (qi < p.Sq) x = *reinterpret_cast<const u32x4*>(qg + (size_t)qi * D + ks * 16 + h * 8);
-    x ^= p.qsign;
+    if constexpr (PRE) {
+      f16x8 v = __builtin_bit_cast(f16x8, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)((float)v[e] * p.cs);
+      x = __builtin_bit_cast(u32x4, v);
+    } else {
+      x ^= p.qsign;
+    }
     qf[ks] = x;
   }
 
@@ -312,9 +336,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_ref = -INFINITY;  // reference maximum of the raw (unscaled) scores
+  // reference maximum of the scores: raw units, or exp2 units when PRE
+  float m_ref = -INFINITY;
   float l_run = 0.f;        // this half's share of the running normaliser
-  const float c = p.c;
+  const float c = PRE ? 1.f : p.c;  // score -> exp2 units
+  bool zero_ref = true;     // PRE: every row of the wave has the reference 0 (or none yet)
 
   // i-th score product of a tile: S^T[32kb.., q] += K[32kb + n][16ks + 8h ..] q[..]
   auto score_mfma = [&](f32x16* sacc, const char* kt, int i) {
@@ -340,6 +366,15 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
       for (int i = 0; i < NSA; ++i) score_mfma(snext, kn, i);
     }
 
+    if constexpr (PRE) {
+      // scores relative to the reference (nothing to do while it is 0)
+      if (!zero_ref) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] -= m_ref;
+      }
+    }
     if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -350,25 +385,47 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
         }
     }
 
-    // tile row max (both halves of the wave)
-    float mx = sacc[0][0];
+    // tile row max (both halves of the wave), in two independent chains
+    float m2[2] = {sacc[0][0], sacc[0][1]};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = max_halves(mx);
+    for (int i = 2; i < 16 * KB; i += 2)
+      m2[(i >> 1) & 1] = max3(m2[(i >> 1) & 1], sacc[i >> 4][i & 15], sacc[i >> 4][(i & 15) + 1]);
+    const float mx = max_halves(fmaxf(m2[0], m2[1]));
 
     // lazy rescale: move the reference only when some row's max grew past the threshold
-    const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c > kRescaleLog2);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
-      m_ref = m_new;
-      l_run *= alpha;
+    if constexpr (PRE) {
+      const bool first = m_ref == -INFINITY;
+      const bool grow = first || mx > kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        // shift of this row's reference, relative to the scores in sacc
+        const float delta = first ? (fabsf(mx) <= kRescaleLog2 ? 0.f : mx) : (grow ? mx : 0.f);
+        const float alpha = first ? 0.f : exp2f(-delta);
+        m_ref = first ? delta : m_ref + delta;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        if (__builtin_amdgcn_ballot_w64(delta != 0.f) != 0) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] -= delta;
+        }
+        zero_ref = __builtin_amdgcn_ballot_w64(m_ref != 0.f) == 0;
+      }
+    } else {
+      const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c > kRescaleLog2);
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
     }
     const float mc = m_ref * c;
 
@@ -381,8 +438,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         const float sv = sacc[u >> 1][8 * (u & 1) + t8];
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -mc));
-        if constexpr (MASK) pe = (sv == -INFINITY) ? 0.f : pe;  // also covers scale == 0
+        float pe;
+        if constexpr (PRE)
+          pe = __builtin_amdgcn_exp2f(sv);  // relative scores, exp2 units
+        else
+          pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -mc));
+        if constexpr (MASK && !PRE) pe = (sv == -INFINITY) ? 0.f : pe;  // also covers scale == 0
         pv[t8] = pe;
       }
 #pragma unroll
@@ -454,20 +515,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     if (j < nt_w) {
       const char* knext = odd ? kb0 : kb1;
       const char* vcur = odd ? vb1 : vb0;
+      // the few tiles past the branch-free loop all take the masked path
+      // (the mask is exact for any tile), which keeps this loop small
       const int k0 = j * BN;
-      const bool next = j + 1 < nt_w;
-      const bool need_mask = (k0 + BN > p.Sk) || (CAUSAL && k0 + BN - 1 > qw0);
-      if (need_mask) {
-        if (next)
-          tile_step(sacc, snext, knext, vcur, k0, Flag<true>{}, Flag<true>{});
-        else
-          tile_step(sacc, snext, knext, vcur, k0, Flag<true>{}, Flag<false>{});
-      } else {
-        if (next)
-          tile_step(sacc, snext, knext, vcur, k0, Flag<false>{}, Flag<true>{});
-        else
-          tile_step(sacc, snext, knext, vcur, k0, Flag<false>{}, Flag<false>{});
-      }
+      if (j + 1 < nt_w)
+        tile_step(sacc, snext, knext, vcur, k0, Flag<true>{}, Flag<true>{});
+      else
+        tile_step(sacc, snext, knext, vcur, k0, Flag<true>{}, Flag<false>{});
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sacc[kb] = snext[kb];
     }
@@ -510,7 +564,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
           w[1] = pack2<BF16>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
           *reinterpret_cast<u32x2*>(og + d0) = w;
         }
-      if (h == 0) p.lse[(size_t)bh * p.Sq + qi] = (m_ref * c + __log2f(l)) * kLn2;
+      if (h == 0) p.lse[(size_t)bh * p.Sq + qi] = (m_ref * c + __log2f(l)) * kLn2;  // c = 1 when PRE
     }
   }
 }
@@ -528,8 +582,11 @@ hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream
   p.n_qblk = (int)((Sq + kBM - 1) / kBM);
   p.n_wg = (int)(BH * p.n_qblk);
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN>),
-                         dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
+  // pre-scale fp16 q when |scale*log2(e)| <= 1, so q*scale*log2(e) cannot overflow
+  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN, false>);
+  if constexpr (!BF16)
+    if (fabsf(p.cs) <= 1.f) fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN, true>);
+  return hipLaunchKernel(fn, dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -576,6 +633,7 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
   p.n_wg = 0;
   p.c = (float)(fabs((double)scale) * 1.4426950408889634);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
+  p.cs = (float)((double)scale * 1.4426950408889634);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = dtype == FA_BF16;
