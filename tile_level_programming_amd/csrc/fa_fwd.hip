@@ -209,6 +209,24 @@ __device__ __forceinline__ void load_rows_to_lds(const uint16_t* g, int k0, int 
 template <bool B>
 struct Flag { static constexpr bool value = B; };
 
+template <int I>
+struct Int { static constexpr int value = I; };
+
+// s_waitcnt vmcnt(n) for n in {0, a, 2a, 3a, 4a} (the counter needs an immediate)
+template <int A>
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n <= 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (n <= A)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(A) : "memory");
+  else if (n <= 2 * A)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * A) : "memory");
+  else if (n <= 3 * A)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * A) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * A) : "memory");
+}
+
 // PRE: q is multiplied by scale*log2(e) (rounded to fp16) when it is loaded,
 // so the score products give exp2-domain logits directly, and the scores a
 // step exponentiates are kept relative to the row's reference.  A row's
@@ -231,16 +249,24 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   static_assert(!(PRE && BF16), "pre-scaling rounds q to fp16");
   static_assert(DK >= NSA, "the early score products must share one 32-key block");
 
-  // K and V stages as four separate arrays: the compiler can then tell that
-  // the loads streaming into one array never alias the reads from another.
+  // A ring of four LDS stages per tensor (tile t in stage t % 4), each a
+  // separate array: the compiler can then tell that the loads streaming into
+  // one stage never alias the reads from another.  Tiles are loaded two steps
+  // before they are read, which hides the load latency of a step.
   __shared__ u32x4 kst0[TILE / 16];
   __shared__ u32x4 kst1[TILE / 16];
+  __shared__ u32x4 kst2[TILE / 16];
+  __shared__ u32x4 kst3[TILE / 16];
   __shared__ u32x4 vst0[TILE / 16];
   __shared__ u32x4 vst1[TILE / 16];
-  char* const kb0 = reinterpret_cast<char*>(kst0);
-  char* const kb1 = reinterpret_cast<char*>(kst1);
-  char* const vb0 = reinterpret_cast<char*>(vst0);
-  char* const vb1 = reinterpret_cast<char*>(vst1);
+  __shared__ u32x4 vst2[TILE / 16];
+  __shared__ u32x4 vst3[TILE / 16];
+  auto kbuf = [&](int t) -> char* {
+    return reinterpret_cast<char*>(t == 0 ? kst0 : t == 1 ? kst1 : t == 2 ? kst2 : kst3);
+  };
+  auto vbuf = [&](int t) -> char* {
+    return reinterpret_cast<char*>(t == 0 ? vst0 : t == 1 ? vst1 : t == 2 ? vst2 : vst3);
+  };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave branches scalar
@@ -273,7 +299,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   if (CAUSAL) j_mask = min(j_mask, (qw0 + 1) / BN);
   // tiles 0 .. j_fast-1 need no mask and have a successor: the branch-free
   // loop runs them in pairs
-  const int j_fast = max(0, min(nt_w - 1, j_mask)) & ~1;
+  // (and the loads they issue, two tiles ahead, all exist: the loop waits
+  // for them with a fixed count)
+  const int j_fast = max(0, min(min(nt_w - 1, j_mask), ntiles - 3)) & ~3;
 
   // ---- tile loads: each lane fetches the global chunk that belongs at its LDS slot
   int offk[NLD], offv[NLD];
@@ -291,9 +319,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     load_rows_to_lds<NLD>(vg, tile * BN, p.Sk, ROWB, buf + wave * 1024, kWaves * 1024, offv);
   };
 
-  issue_k(0, kb0);
-  issue_v(0, vb0);
-  if (ntiles > 1) issue_k(1, kb1);
+  // K 0 first (the prologue's scores need it), then K 1, V 0, K 2, V 1
+  issue_k(0, kbuf(0));
+  int loads_after_k0 = 0;
+  if (ntiles > 1) { issue_k(1, kbuf(1)); loads_after_k0 += NLD; }
+  issue_v(0, vbuf(0));
+  loads_after_k0 += NLD;
+  if (ntiles > 2) { issue_k(2, kbuf(2)); loads_after_k0 += NLD; }
+  if (ntiles > 1) { issue_v(1, vbuf(1)); loads_after_k0 += NLD; }
 
   // ---- Q fragments: B operands of S^T = K Q^T; lane holds q[qi][16*ks + 8*h .. +8]
   u32x4 qf[DK];
@@ -493,28 +526,38 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     }
   };
 
-  // K tile j+1 and V tile j resident for every wave; every wave is done
-  // with K tile j (read for the scores last step) and V tile j-1; start the
-  // loads of K tile j+2 and V tile j+1
-  auto stage = [&](int j, char* kfree, char* vnext) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 2 < ntiles) issue_k(j + 2, kfree);
-    if (j + 1 < ntiles) issue_v(j + 1, vnext);
+  // Step j reads K tile j+1 and V tile j, loaded at step j-2 (or before the
+  // loop): after the wait, the barrier makes them visible to every wave and
+  // guarantees that every wave is done with K tile j-1 and V tile j-2, whose
+  // stages take K tile j+3 and V tile j+2.
+  auto issue_next = [&](int j) {
+    if (j + 3 < ntiles) issue_k(j + 3, kbuf((j + 3) & 3));
+    if (j + 2 < ntiles) issue_v(j + 2, vbuf((j + 2) & 3));
   };
-  auto step_fast = [&](int j, char* kfree, const char* knext, const char* vcur, char* vnext, f32x16* sacc,
-                       f32x16* snext) {
-    stage(j, kfree, vnext);
-    tile_step(sacc, snext, knext, vcur, j * BN, Flag<false>{}, Flag<true>{});
+  // branch-free step (compile-time stages): the previous step issued 2*NLD loads
+  auto step_fast = [&](int j, auto jm4_tag, f32x16* sacc, f32x16* snext) {
+    constexpr int jm = decltype(jm4_tag)::value;  // j % 4
+    // the wait and the barrier in one asm statement with a memory clobber:
+    // no LDS access moves across it, and no release fence makes the compiler
+    // wait for the loads still in flight (they target other stages); every
+    // LDS read of the previous step has returned (lgkmcnt) before any wave
+    // may overwrite its stage
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * NLD) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue_k(j + 3, kbuf((jm + 3) & 3));
+    issue_v(j + 2, vbuf((jm + 2) & 3));
+    tile_step(sacc, snext, kbuf((jm + 1) & 3), vbuf(jm), j * BN, Flag<false>{}, Flag<true>{});
   };
   // any tile: masked or not, with or without a successor; the scores of the
   // successor land in snext and are moved to sacc
   auto step = [&](int j, f32x16* sacc, f32x16* snext) {
-    const bool odd = j & 1;
-    stage(j, odd ? kb1 : kb0, odd ? vb0 : vb1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue_next(j);
     if (j < nt_w) {
-      const char* knext = odd ? kb0 : kb1;
-      const char* vcur = odd ? vb1 : vb0;
+      const char* knext = kbuf((j + 1) & 3);
+      const char* vcur = vbuf(j & 3);
       // the few tiles past the branch-free loop all take the masked path
       // (the mask is exact for any tile), which keeps this loop small
       const int k0 = j * BN;
@@ -533,18 +576,21 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) sa[kb][r] = 0.f;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vm<NLD>(loads_after_k0);  // K tile 0 has landed
   __syncthreads();
   if (nt_w > 0) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) score_mfma(sa, kb0, i);
+    for (int i = 0; i < NS; ++i) score_mfma(sa, kbuf(0), i);
   }
 
-  // K tile t lives in kb[t&1], V tile t in vb[t&1]
+  // (the fast loop's first step waits for all but 2*NLD loads: K 2 and V 1
+  // may still be in flight, K 1 and V 0 have landed)
   int j = 0;
-  for (; j < j_fast; j += 2) {
-    step_fast(j, kb0, kb1, vb0, vb1, sa, sb);
-    step_fast(j + 1, kb1, kb0, vb1, vb0, sb, sa);
+  for (; j < j_fast; j += 4) {
+    step_fast(j, Int<0>{}, sa, sb);
+    step_fast(j + 1, Int<1>{}, sb, sa);
+    step_fast(j + 2, Int<2>{}, sa, sb);
+    step_fast(j + 3, Int<3>{}, sb, sa);
   }
   for (; j < ntiles; ++j) step(j, sa, sb);
 
