@@ -180,6 +180,27 @@ def test_large_logits_rescaling(torch_dev, fa, oracle_mod):
         full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(128), causal, "sigma4")
 
 
+def _bits_to_f32(bits, dtype):
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float32)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16"), (64, "bf16"), (128, "f16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_logits(torch_dev, fa, oracle_mod, D, dtype, causal):
+    # keys scaled up along the sequence: each row's maximum keeps growing,
+    # so the kernel's reference has to move many times, in the branch-free
+    # steps and in the masked tail, both before and after a tile's products
+    Sq, Sk = 300, 2000
+    q = fi.tensor_bits(24, "q", (1, 2, Sq, D), dtype, 2.0)
+    k0 = _bits_to_f32(fi.tensor_bits(24, "k", (1, 2, Sk, D), dtype), dtype)
+    ramp = (0.25 + 6.0 * np.arange(Sk, dtype=np.float32) / Sk)[None, None, :, None]
+    k = fi.f32_to_bits(k0 * ramp, dtype)
+    v = fi.tensor_bits(24, "v", (1, 2, Sk, D), dtype)
+    full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(D), causal, f"rising {D} {dtype}")
+
+
 # --- properties checkable without the oracle ---------------------------------
 
 

@@ -76,7 +76,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleLog2 = 8.0f;            // lazy-rescale threshold, exp2 units
+// A lane's sum of P over one tile above this makes its wave move the
+// reference (and rescale); below it every P of the tile is at most this,
+// far inside the 16-bit range (fp16 max 65504).
+constexpr float kSumBound = 4096.0f;
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr int kWaves = 4;                       // waves per work-group
 constexpr int kBM = 32 * kWaves;                // queries per work-group
@@ -97,7 +100,6 @@ struct Params {
   int n_wg;        // total work-groups
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 when scale < 0 (q is negated on load), else 0
-  float cs;        // scale * log2(e), by which q is multiplied on load when pre-scaling
 };
 
 template <bool BF16>
@@ -126,18 +128,13 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   }
 }
 
-// acc + (sum of the two fp16 values packed in w), accumulated in f32.
-__device__ __forceinline__ float add_pair_f16(uint32_t w, float acc) {
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
-}
-
 // v_permlane32_swap exchanges the two 32-lane halves of a wave: afterwards
 // the pair holds, in every lane, the values of lane l%32 and lane l%32+32.
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
                                                   __builtin_bit_cast(uint32_t, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)r[0]),
+                                       __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
@@ -145,13 +142,11 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-// max(a, b, c) as one v_max3_f32.  Written out because fmaxf would first
-// quiet each input (the kernel runs with IEEE mode on), one extra instruction
-// per input; a NaN score still reaches the output through its exponential.
+// max(a, b, c) with NaN propagation (IEEE 754-2019 maximum): one
+// v_maximum3_f32, with no quieting of the inputs that fmaxf would need in
+// IEEE mode.  A NaN score makes its row's maximum, and so its output, NaN.
 __device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 __device__ __forceinline__ u32x4 lds_read_b128(const char* base, int off) {
@@ -194,13 +189,16 @@ __device__ __forceinline__ int vsw(int r) {
 // Stream NLD 1 KB blocks of one tensor's rows k0.. into LDS.  Lane l of
 // block i fills bytes 16l..16l+15 of the block at dst + i*stride, reading the
 // bytes at off[i] of the rows from key k0 on; the buffer range ends at key
-// Sk, so rows past it arrive as zeros.
+// Sk, so rows past it arrive as zeros.  A tile wholly past the keys gets an
+// empty range: its loads touch no memory, write zeros and still count in
+// vmcnt, which keeps the number of loads in flight the same every step.
 template <int NLD>
 __device__ __forceinline__ void load_rows_to_lds(const uint16_t* g, int k0, int Sk, int rowb, char* dst,
                                                  int stride, const int* off) {
-  const uint32_t bytes = (uint32_t)(Sk - k0) * (uint32_t)rowb;
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)g + (size_t)k0 * rowb), (short)0, bytes, kBufferWord3);
+  const bool any = k0 < Sk;
+  const uint32_t bytes = any ? (uint32_t)(Sk - k0) * (uint32_t)rowb : 0u;
+  const char* base = (const char*)g + (any ? (size_t)k0 * rowb : 0);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufferWord3);
 #pragma unroll
   for (int i = 0; i < NLD; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * stride), 16, off[i], 0, 0, 0);
@@ -212,28 +210,7 @@ struct Flag { static constexpr bool value = B; };
 template <int I>
 struct Int { static constexpr int value = I; };
 
-// s_waitcnt vmcnt(n) for n in {0, a, 2a, 3a, 4a} (the counter needs an immediate)
-template <int A>
-__device__ __forceinline__ void wait_vm(int n) {
-  if (n <= 0)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (n <= A)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(A) : "memory");
-  else if (n <= 2 * A)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * A) : "memory");
-  else if (n <= 3 * A)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * A) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * A) : "memory");
-}
-
-// PRE: q is multiplied by scale*log2(e) (rounded to fp16) when it is loaded,
-// so the score products give exp2-domain logits directly, and the scores a
-// step exponentiates are kept relative to the row's reference.  A row's
-// first reference is 0 when its first maximum lies within +-kRescaleLog2 of
-// 0 (moderate logits); while every row of a wave has the reference 0,
-// P = exp2(s) needs no subtraction at all.
-template <int D, bool BF16, bool CAUSAL, int BN, bool PRE>
+template <int D, bool BF16, bool CAUSAL, int BN>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                     // bytes per row
@@ -246,7 +223,6 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int NS = KB * DK;                     // score products per tile
   constexpr int NSA = NS / 2;                     // of which issued ahead of the row maximum
   static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over the waves");
-  static_assert(!(PRE && BF16), "pre-scaling rounds q to fp16");
   static_assert(DK >= NSA, "the early score products must share one 32-key block");
 
   // A ring of four LDS stages per tensor (tile t in stage t % 4), each a
@@ -261,10 +237,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   __shared__ u32x4 vst1[TILE / 16];
   __shared__ u32x4 vst2[TILE / 16];
   __shared__ u32x4 vst3[TILE / 16];
-  auto kbuf = [&](int t) -> char* {
+  auto kbuf = [&](int t) __attribute__((always_inline)) -> char* {
     return reinterpret_cast<char*>(t == 0 ? kst0 : t == 1 ? kst1 : t == 2 ? kst2 : kst3);
   };
-  auto vbuf = [&](int t) -> char* {
+  auto vbuf = [&](int t) __attribute__((always_inline)) -> char* {
     return reinterpret_cast<char*>(t == 0 ? vst0 : t == 1 ? vst1 : t == 2 ? vst2 : vst3);
   };
 
@@ -297,11 +273,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   // this wave's first query
   int j_mask = p.Sk / BN;
   if (CAUSAL) j_mask = min(j_mask, (qw0 + 1) / BN);
-  // tiles 0 .. j_fast-1 need no mask and have a successor: the branch-free
-  // loop runs them in pairs
-  // (and the loads they issue, two tiles ahead, all exist: the loop waits
-  // for them with a fixed count)
-  const int j_fast = max(0, min(min(nt_w - 1, j_mask), ntiles - 3)) & ~3;
+  // steps 0 .. j_fast-1 run branch-free: step j exponentiates tile j+1
+  // (which must need no mask) and forms the scores of tile j+2 (which must
+  // exist); a multiple of 4 steps, one per LDS stage
+  const int j_fast = max(0, min(j_mask - 1, nt_w - 2)) & ~3;
 
   // ---- tile loads: each lane fetches the global chunk that belongs at its LDS slot
   int offk[NLD], offv[NLD];
@@ -312,21 +287,22 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     offk[i] = r * ROWB + ((pc ^ ksw<D>(r)) << 4);
     offv[i] = r * ROWB + ((pc ^ vsw<D>(r)) << 4);
   }
-  auto issue_k = [&](int tile, char* buf) {
+  auto issue_k = [&](int tile, char* buf) __attribute__((always_inline)) {
     load_rows_to_lds<NLD>(kg, tile * BN, p.Sk, ROWB, buf + wave * 1024, kWaves * 1024, offk);
   };
-  auto issue_v = [&](int tile, char* buf) {
+  auto issue_v = [&](int tile, char* buf) __attribute__((always_inline)) {
     load_rows_to_lds<NLD>(vg, tile * BN, p.Sk, ROWB, buf + wave * 1024, kWaves * 1024, offv);
   };
 
-  // K 0 first (the prologue's scores need it), then K 1, V 0, K 2, V 1
+  // K 0 and K 1 first (the prologue's scores), then K 2 and V 0 (step 0),
+  // K 3 and V 1 (step 1); every step then issues 2*NLD loads (K j+4, V j+2),
+  // past the keys included, so each wait has a fixed count
   issue_k(0, kbuf(0));
-  int loads_after_k0 = 0;
-  if (ntiles > 1) { issue_k(1, kbuf(1)); loads_after_k0 += NLD; }
+  issue_k(1, kbuf(1));
+  issue_k(2, kbuf(2));
   issue_v(0, vbuf(0));
-  loads_after_k0 += NLD;
-  if (ntiles > 2) { issue_k(2, kbuf(2)); loads_after_k0 += NLD; }
-  if (ntiles > 1) { issue_v(1, vbuf(1)); loads_after_k0 += NLD; }
+  issue_k(3, kbuf(3));
+  issue_v(1, vbuf(1));
 
   // ---- Q fragments: B operands of S^T = K Q^T; lane holds q[qi][16*ks + 8*h .. +8]
   u32x4 qf[DK];
@@ -334,14 +310,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int ks = 0; ks < DK; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (qi < p.Sq) x = *reinterpret_cast<const u32x4*>(qg + (size_t)qi * D + ks * 16 + h * 8);
-    if constexpr (PRE) {
-      f16x8 v = __builtin_bit_cast(f16x8, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (_Float16)((float)v[e] * p.cs);
-      x = __builtin_bit_cast(u32x4, v);
-    } else {
-      x ^= p.qsign;
-    }
+    x ^= p.qsign;
     qf[ks] = x;
   }
 
@@ -369,230 +338,219 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  // reference maximum of the scores: raw units, or exp2 units when PRE
-  float m_ref = -INFINITY;
+  float m_ref = -INFINITY;  // reference maximum of the raw scores
   float l_run = 0.f;        // this half's share of the running normaliser
-  const float c = PRE ? 1.f : p.c;  // score -> exp2 units
-  bool zero_ref = true;     // PRE: every row of the wave has the reference 0 (or none yet)
+  const float c = p.c;      // raw score -> exp2 units
 
   // i-th score product of a tile: S^T[32kb.., q] += K[32kb + n][16ks + 8h ..] q[..]
-  auto score_mfma = [&](f32x16* sacc, const char* kt, int i) {
-    const int kb = i / DK, ks = i % DK;
-    sacc[kb] = mfma_32x32x16<BF16>(lds_read_b128(kt, koff[ks] + kb * 32 * ROWB), qf[ks], sacc[kb]);
+  auto k_frag = [&](const char* kt, int i) __attribute__((always_inline)) { return lds_read_b128(kt, koff[i % DK] + (i / DK) * 32 * ROWB); };
+  // V^T fragment of the P.V product (16-key slice u, d block db)
+  auto v_frag = [&](const char* vt, int u, int db) __attribute__((always_inline)) {
+    const char* vp = vt + voff[db] + 16 * u * ROWB;
+    const u32x2 lo = lds_read_tr16(vp);
+    const u32x2 hi = lds_read_tr16(vp + 8 * ROWB);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto zero_scores = [&](f32x16* sacc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
   };
 
-  // One key tile: softmax and P.V of tile j (scores in sacc, V tile at vt),
-  // and, when NEXT, the scores of tile j+1 into snext from the K tile at kn.
-  // sacc[kb][r] = score(query qi, key k0 + 32kb + 8(r/4) + 4h + r%4).
-  auto tile_step = [&](f32x16* sacc, f32x16* snext, const char* kn, const char* vt, int k0, auto mask_tag,
-                       auto next_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool NEXT = decltype(next_tag)::value;
-
-    // the first half of the next tile's score products runs under the row max
-    if constexpr (NEXT) {
+  // Scores past the keys or (causal) above the diagonal become -inf.
+  // sacc[kb][r] = score(qi, k0 + 32kb + 8(r/4) + 4h + r%4).
+  auto apply_mask = [&](f32x16* sacc, int k0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) snext[kb][r] = 0.f;
-#pragma unroll
-      for (int i = 0; i < NSA; ++i) score_mfma(snext, kn, i);
-    }
-
-    if constexpr (PRE) {
-      // scores relative to the reference (nothing to do while it is 0)
-      if (!zero_ref) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] -= m_ref;
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= p.Sk || (CAUSAL && key > qi)) sacc[kb][r] = -INFINITY;
       }
-    }
-    if constexpr (MASK) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= p.Sk || (CAUSAL && key > qi)) sacc[kb][r] = -INFINITY;
-        }
-    }
+  };
 
-    // tile row max (both halves of the wave), in two independent chains
+  // Row maximum of a tile's scores (this lane's query, both halves of the
+  // wave), in two independent chains of v_maximum3.
+  auto tile_max = [&](const f32x16* sacc) __attribute__((always_inline)) -> float {
     float m2[2] = {sacc[0][0], sacc[0][1]};
 #pragma unroll
     for (int i = 2; i < 16 * KB; i += 2)
       m2[(i >> 1) & 1] = max3(m2[(i >> 1) & 1], sacc[i >> 4][i & 15], sacc[i >> 4][(i & 15) + 1]);
-    const float mx = max_halves(fmaxf(m2[0], m2[1]));
+    return max_halves(__builtin_elementwise_maximum(m2[0], m2[1]));
+  };
 
-    // lazy rescale: move the reference only when some row's max grew past the threshold
-    if constexpr (PRE) {
-      const bool first = m_ref == -INFINITY;
-      const bool grow = first || mx > kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        // shift of this row's reference, relative to the scores in sacc
-        const float delta = first ? (fabsf(mx) <= kRescaleLog2 ? 0.f : mx) : (grow ? mx : 0.f);
-        const float alpha = first ? 0.f : exp2f(-delta);
-        m_ref = first ? delta : m_ref + delta;
-        l_run *= alpha;
+  auto scale_o = [&](float alpha) __attribute__((always_inline)) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        if (__builtin_amdgcn_ballot_w64(delta != 0.f) != 0) {
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] -= delta;
-        }
-        zero_ref = __builtin_amdgcn_ballot_w64(m_ref != 0.f) == 0;
-      }
-    } else {
-      const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c > kRescaleLog2);
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
-        m_ref = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-    }
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+  };
+
+  // P = exp2(s*c - m*c) against the current reference, packed to 16 bits
+  // into pout; returns this lane's sum of the tile's P (fp32: v_add_f32 runs
+  // beside the matrix instructions, a v_dot2 of the packed values would not).
+  auto tile_exp = [&](const f32x16* sacc, u32x4* pout, auto mask_tag) __attribute__((always_inline)) -> float {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const float mc = m_ref * c;
-
-    // P = exp2(s*c - m*c), packed to 16 bits; running sum
-    u32x4 pf[NU];
-    float psum = l_run;
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       float pv[8];
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         const float sv = sacc[u >> 1][8 * (u & 1) + t8];
-        float pe;
-        if constexpr (PRE)
-          pe = __builtin_amdgcn_exp2f(sv);  // relative scores, exp2 units
-        else
-          pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -mc));
-        if constexpr (MASK && !PRE) pe = (sv == -INFINITY) ? 0.f : pe;  // also covers scale == 0
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -mc));
+        if constexpr (MASK) pe = (sv == -INFINITY) ? 0.f : pe;  // also covers scale == 0
         pv[t8] = pe;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pf[u][e] = pack2<BF16>(pv[2 * e], pv[2 * e + 1]);
-        // fp16 rounds P to within 2^-12, so summing the rounded values keeps the
-        // normaliser (and lse) accurate; bf16 rounding (2^-9) would not, so bf16
-        // sums the fp32 values.
-        if constexpr (BF16)
-          psum += pv[2 * e] + pv[2 * e + 1];
-        else
-          psum = add_pair_f16(pf[u][e], psum);
+        pout[u][e] = pack2<BF16>(pv[2 * e], pv[2 * e + 1]);
+        ps[e & 1] += pv[2 * e] + pv[2 * e + 1];
       }
     }
-    l_run = psum;
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int u = 0; u < NU; ++u)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const char* vp = vt + voff[db] + 16 * u * ROWB;
-        const u32x2 lo = lds_read_tr16(vp);
-        const u32x2 hi = lds_read_tr16(vp + 8 * ROWB);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = mfma_32x32x16<BF16>(a, pf[u], oacc[db]);
-      }
-
-    // the second half of the next tile's score products
-    if constexpr (NEXT) {
-#pragma unroll
-      for (int i = NSA; i < NS; ++i) score_mfma(snext, kn, i);
-    }
-
-    // Interleave: one matrix instruction, then a run of vector instructions
-    // and LDS reads, so the wave keeps the matrix unit busy while it
-    // exponentiates.
-    constexpr int NMF = NU * DB + (NEXT ? NS - NSA : 0);
-    constexpr int NVALU = NU * (8 + 8 + 4 + (BF16 ? 8 : 4));
-    constexpr int VPM = (NVALU + NMF - 1) / NMF;
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-#pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, VPM, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-    }
+    return ps[0] + ps[1];
   };
 
-  // Step j reads K tile j+1 and V tile j, loaded at step j-2 (or before the
-  // loop): after the wait, the barrier makes them visible to every wave and
-  // guarantees that every wave is done with K tile j-1 and V tile j-2, whose
-  // stages take K tile j+3 and V tile j+2.
-  auto issue_next = [&](int j) {
-    if (j + 3 < ntiles) issue_k(j + 3, kbuf((j + 3) & 3));
-    if (j + 2 < ntiles) issue_v(j + 2, vbuf((j + 2) & 3));
+  // The reference moves to the row's running maximum: for the first tile,
+  // and when some lane's sum over a tile exceeded kSumBound (then its P are
+  // no longer known to be small).  O (which holds the products of the
+  // earlier tiles) and the running sum are rescaled, and the tile is
+  // exponentiated again.  Masked scores are -inf already.
+  auto reref = [&](const f32x16* sacc, u32x4* pout) __attribute__((always_inline)) {
+    const float m_new = fmaxf(m_ref, tile_max(sacc));
+    const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
+    m_ref = m_new;
+    scale_o(alpha);
+    l_run = l_run * alpha + tile_exp(sacc, pout, Flag<true>{});
   };
-  // branch-free step (compile-time stages): the previous step issued 2*NLD loads
-  auto step_fast = [&](int j, auto jm4_tag, f32x16* sacc, f32x16* snext) {
+  // set by a step whose exponentials hit the bound: the next step, before
+  // its products, re-references that tile (its scores are still in the
+  // buffer the next step fills with new scores, and its P is the next
+  // step's pcur)
+  bool redo = false;
+
+  // One step j of the pipeline, with K tile j+2 at kt and V tile j at vt:
+  //   matrix unit: scores of tile j+2 (into snext), and O^T += V^T P^T with
+  //                P of tile j (pcur, exponentiated by the previous step);
+  //   vector unit: exponentials of tile j+1 (scores in scur, formed by the
+  //                previous step) into pnext, against the current reference.
+  // The two streams share no data, so the interleaved instructions never
+  // wait on each other; no row maximum is needed unless a tile's P grows
+  // too large (then the next step re-references it first).
+  auto step_fast = [&](int j, auto jm4_tag, f32x16* scur, f32x16* snext, u32x4* pcur,
+                       u32x4* pnext) __attribute__((always_inline)) {
     constexpr int jm = decltype(jm4_tag)::value;  // j % 4
     // the wait and the barrier in one asm statement with a memory clobber:
     // no LDS access moves across it, and no release fence makes the compiler
     // wait for the loads still in flight (they target other stages); every
     // LDS read of the previous step has returned (lgkmcnt) before any wave
-    // may overwrite its stage
+    // may overwrite its stage.  Loads of the previous step may stay in flight.
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * NLD) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    issue_k(j + 3, kbuf((jm + 3) & 3));
+    issue_k(j + 4, kbuf(jm));
     issue_v(j + 2, vbuf((jm + 2) & 3));
-    tile_step(sacc, snext, kbuf((jm + 1) & 3), vbuf(jm), j * BN, Flag<false>{}, Flag<true>{});
-  };
-  // any tile: masked or not, with or without a successor; the scores of the
-  // successor land in snext and are moved to sacc
-  auto step = [&](int j, f32x16* sacc, f32x16* snext) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    issue_next(j);
-    if (j < nt_w) {
-      const char* knext = kbuf((j + 1) & 3);
-      const char* vcur = vbuf(j & 3);
-      // the few tiles past the branch-free loop all take the masked path
-      // (the mask is exact for any tile), which keeps this loop small
-      const int k0 = j * BN;
-      if (j + 1 < nt_w)
-        tile_step(sacc, snext, knext, vcur, k0, Flag<true>{}, Flag<true>{});
-      else
-        tile_step(sacc, snext, knext, vcur, k0, Flag<true>{}, Flag<false>{});
+    const char* kt = kbuf((jm + 2) & 3);
+    const char* vt = vbuf(jm);
+
+    if (redo) reref(snext, pcur);  // (snext still holds the scores of tile j)
+    zero_scores(snext);
+    const float ts = tile_exp(scur, pnext, Flag<false>{});
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) sacc[kb] = snext[kb];
+    for (int i = 0; i < NS; ++i) snext[i / DK] = mfma_32x32x16<BF16>(k_frag(kt, i), qf[i % DK], snext[i / DK]);
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = mfma_32x32x16<BF16>(v_frag(vt, u, db), pcur[u], oacc[db]);
+    {
+      // one matrix instruction, then a run of vector instructions and two
+      // LDS reads (the first K fragments are read up front)
+      constexpr int NMF = NS + NU * DB;
+      constexpr int NV = NU * (8 + 8 + 4 + 8);
+      constexpr int VPM = (NV + NMF - 1) / NMF;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, VPM, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+    }
+    // pin the packed P to this block: the packing would otherwise sink past
+    // the next step's redo branch, out of the interleaved schedule
+#pragma unroll
+    for (int u = 0; u < NU; ++u) asm volatile("" ::"v"(pnext[u]));
+    redo = __builtin_amdgcn_ballot_w64(ts > kSumBound) != 0;
+    if (!redo) l_run += ts;
+  };
+
+  // Any step: the tiles may need masks, and tile j+1 or j+2 may not exist
+  // for this wave.
+  auto step_any = [&](int j, f32x16* scur, f32x16* snext, u32x4* pcur, u32x4* pnext) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD) : "memory");
+    __syncthreads();
+    issue_k(j + 4, kbuf((j + 4) & 3));
+    issue_v(j + 2, vbuf((j + 2) & 3));
+    if (j < nt_w) {
+      const char* kt = kbuf((j + 2) & 3);
+      const char* vt = vbuf(j & 3);
+      if (redo) reref(snext, pcur);
+      if (j + 2 < nt_w) {
+        zero_scores(snext);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) snext[i / DK] = mfma_32x32x16<BF16>(k_frag(kt, i), qf[i % DK], snext[i / DK]);
+      }
+      float ts = 0.f;
+      if (j + 1 < nt_w) {
+        apply_mask(scur, (j + 1) * BN);
+        ts = tile_exp(scur, pnext, Flag<true>{});
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] = mfma_32x32x16<BF16>(v_frag(vt, u, db), pcur[u], oacc[db]);
+      redo = __builtin_amdgcn_ballot_w64(ts > kSumBound) != 0;
+      if (!redo) l_run += ts;
     }
   };
 
-  // scores of tile 0
+  // ---- prologue: scores of tiles 0 and 1, P of tile 0
   f32x16 sa[KB], sb[KB];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sa[kb][r] = 0.f;
-  wait_vm<NLD>(loads_after_k0);  // K tile 0 has landed
+  u32x4 pa[NU], pb[NU];
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NLD) : "memory");  // K 0 and K 1 have landed
   __syncthreads();
   if (nt_w > 0) {
+    zero_scores(sa);
+    zero_scores(sb);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) score_mfma(sa, kbuf(0), i);
+    for (int i = 0; i < NS; ++i) sa[i / DK] = mfma_32x32x16<BF16>(k_frag(kbuf(0), i), qf[i % DK], sa[i / DK]);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) sb[i / DK] = mfma_32x32x16<BF16>(k_frag(kbuf(1), i), qf[i % DK], sb[i / DK]);
+    // (every row's first maximum is finite: key 0 is never masked)
+    apply_mask(sa, 0);
+    reref(sa, pa);
   }
 
-  // (the fast loop's first step waits for all but 2*NLD loads: K 2 and V 1
-  // may still be in flight, K 1 and V 0 have landed)
+  // step j: scores of tile j+1 in sb (j even) or sa (j odd), P of tile j in
+  // pa (j even) or pb (j odd)
   int j = 0;
   for (; j < j_fast; j += 4) {
-    step_fast(j, Int<0>{}, sa, sb);
-    step_fast(j + 1, Int<1>{}, sb, sa);
-    step_fast(j + 2, Int<2>{}, sa, sb);
-    step_fast(j + 3, Int<3>{}, sb, sa);
+    step_fast(j, Int<0>{}, sb, sa, pa, pb);
+    step_fast(j + 1, Int<1>{}, sa, sb, pb, pa);
+    step_fast(j + 2, Int<2>{}, sb, sa, pa, pb);
+    step_fast(j + 3, Int<3>{}, sa, sb, pb, pa);
   }
-  for (; j < ntiles; ++j) step(j, sa, sb);
+  // (j is a multiple of 4 here)
+  for (; j < ntiles; j += 2) {
+    step_any(j, sb, sa, pa, pb);
+    if (j + 1 < ntiles) step_any(j + 1, sa, sb, pb, pa);
+  }
+
+  // the last steps' loads (past the keys) are still in flight: let them land
+  // before the work-group's LDS can be handed to another
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: normalise, round, store O rows and lse
   if (qw0 < p.Sq) {
@@ -610,7 +568,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
           w[1] = pack2<BF16>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
           *reinterpret_cast<u32x2*>(og + d0) = w;
         }
-      if (h == 0) p.lse[(size_t)bh * p.Sq + qi] = (m_ref * c + __log2f(l)) * kLn2;  // c = 1 when PRE
+      if (h == 0) p.lse[(size_t)bh * p.Sq + qi] = (m_ref * c + __log2f(l)) * kLn2;
     }
   }
 }
@@ -628,10 +586,7 @@ hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream
   p.n_qblk = (int)((Sq + kBM - 1) / kBM);
   p.n_wg = (int)(BH * p.n_qblk);
   void* args[] = {&p};
-  // pre-scale fp16 q when |scale*log2(e)| <= 1, so q*scale*log2(e) cannot overflow
-  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN, false>);
-  if constexpr (!BF16)
-    if (fabsf(p.cs) <= 1.f) fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN, true>);
+  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN>);
   return hipLaunchKernel(fn, dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
 }
 
@@ -679,7 +634,6 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
   p.n_wg = 0;
   p.c = (float)(fabs((double)scale) * 1.4426950408889634);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
-  p.cs = (float)((double)scale * 1.4426950408889634);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = dtype == FA_BF16;
