@@ -100,6 +100,7 @@ struct Params {
   int n_wg;        // total work-groups
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 when scale < 0 (q is negated on load), else 0
+  float cs;        // scale * log2(e), by which q is multiplied on load when pre-scaling
 };
 
 template <bool BF16>
@@ -210,7 +211,10 @@ struct Flag { static constexpr bool value = B; };
 template <int I>
 struct Int { static constexpr int value = I; };
 
-template <int D, bool BF16, bool CAUSAL, int BN>
+// PRE (fp16 only): q is multiplied by scale*log2(e) (rounded to fp16) as it
+// is loaded, so the score products give exp2-domain logits and P = exp2(s)
+// needs no instruction besides the exponential.
+template <int D, bool BF16, bool CAUSAL, int BN, bool PRE>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                     // bytes per row
@@ -223,6 +227,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int NS = KB * DK;                     // score products per tile
   constexpr int NSA = NS / 2;                     // of which issued ahead of the row maximum
   static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over the waves");
+  static_assert(!(PRE && BF16), "pre-scaling rounds q to fp16");
   static_assert(DK >= NSA, "the early score products must share one 32-key block");
 
   // A ring of four LDS stages per tensor (tile t in stage t % 4), each a
@@ -310,7 +315,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int ks = 0; ks < DK; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (qi < p.Sq) x = *reinterpret_cast<const u32x4*>(qg + (size_t)qi * D + ks * 16 + h * 8);
-    x ^= p.qsign;
+    if constexpr (PRE) {
+      f16x8 v = __builtin_bit_cast(f16x8, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)((float)v[e] * p.cs);
+      x = __builtin_bit_cast(u32x4, v);
+    } else {
+      x ^= p.qsign;
+    }
     qf[ks] = x;
   }
 
@@ -338,9 +350,18 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_ref = -INFINITY;  // reference maximum of the raw scores
+  // The scores in registers are relative to a per-row reference m_ref
+  // (score units: raw, or exp2 units when PRE): every score product starts
+  // from negm = -m_ref in all 16 accumulator slots instead of from 0, so
+  // the subtraction costs no instruction.
+  float m_ref = 0.f;
   float l_run = 0.f;        // this half's share of the running normaliser
-  const float c = p.c;      // raw score -> exp2 units
+  const float c = PRE ? 1.f : p.c;  // score -> exp2 units
+  f32x16 negm;
+  auto set_negm = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
+  };
 
   // i-th score product of a tile: S^T[32kb.., q] += K[32kb + n][16ks + 8h ..] q[..]
   auto k_frag = [&](const char* kt, int i) __attribute__((always_inline)) { return lds_read_b128(kt, koff[i % DK] + (i / DK) * 32 * ROWB); };
@@ -351,11 +372,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     const u32x2 hi = lds_read_tr16(vp + 8 * ROWB);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
-  auto zero_scores = [&](f32x16* sacc) __attribute__((always_inline)) {
+  // scores of the K tile at kt relative to the reference: each 32-key block
+  // is a chain of DK products starting from negm
+  auto score_tile = [&](f32x16* sacc, const char* kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    for (int i = 0; i < NS; ++i)
+      sacc[i / DK] = mfma_32x32x16<BF16>(k_frag(kt, i), qf[i % DK], i % DK == 0 ? negm : sacc[i / DK]);
   };
 
   // Scores past the keys or (causal) above the diagonal become -inf.
@@ -387,12 +409,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
   };
 
-  // P = exp2(s*c - m*c) against the current reference, packed to 16 bits
+  // P = exp2(s*c) of the relative scores (PRE: exp2(s)), packed to 16 bits
   // into pout; returns this lane's sum of the tile's P (fp32: v_add_f32 runs
   // beside the matrix instructions, a v_dot2 of the packed values would not).
   auto tile_exp = [&](const f32x16* sacc, u32x4* pout, auto mask_tag) __attribute__((always_inline)) -> float {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const float mc = m_ref * c;
     float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -400,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         const float sv = sacc[u >> 1][8 * (u & 1) + t8];
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -mc));
+        float pe = __builtin_amdgcn_exp2f(PRE ? sv : sv * c);
         if constexpr (MASK) pe = (sv == -INFINITY) ? 0.f : pe;  // also covers scale == 0
         pv[t8] = pe;
       }
@@ -413,17 +434,26 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     return ps[0] + ps[1];
   };
 
-  // The reference moves to the row's running maximum: for the first tile,
-  // and when some lane's sum over a tile exceeded kSumBound (then its P are
-  // no longer known to be small).  O (which holds the products of the
-  // earlier tiles) and the running sum are rescaled, and the tile is
-  // exponentiated again.  Masked scores are -inf already.
-  auto reref = [&](const f32x16* sacc, u32x4* pout) __attribute__((always_inline)) {
-    const float m_new = fmaxf(m_ref, tile_max(sacc));
-    const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f((m_ref - m_new) * c);
-    m_ref = m_new;
+  // The reference moves up to the row's running maximum when some lane's
+  // sum over a tile exceeded kSumBound (then its P are no longer known to be
+  // small).  st: that tile's scores, exponentiated again into pout; snx: the
+  // next tile's scores, formed against the old reference.  O (which holds
+  // the products of the earlier tiles) and the running sum are rescaled.
+  // Masked scores are -inf already.
+  auto reref = [&](f32x16* st, u32x4* pout, f32x16* snx) __attribute__((always_inline)) {
+    const float delta = fmaxf(tile_max(st), 0.f);
+    m_ref += delta;
+    set_negm();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st[kb][r] -= delta;
+        snx[kb][r] -= delta;
+      }
+    const float alpha = exp2f(-delta * c);
     scale_o(alpha);
-    l_run = l_run * alpha + tile_exp(sacc, pout, Flag<true>{});
+    l_run = l_run * alpha + tile_exp(st, pout, Flag<true>{});
   };
   // set by a step whose exponentials hit the bound: the next step, before
   // its products, re-references that tile (its scores are still in the
@@ -439,6 +469,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   // The two streams share no data, so the interleaved instructions never
   // wait on each other; no row maximum is needed unless a tile's P grows
   // too large (then the next step re-references it first).
+  // K fragments read one step ahead by the branch-free steps
+  constexpr int NPF = NS;
+  u32x4 kpre[NPF];
   auto step_fast = [&](int j, auto jm4_tag, f32x16* scur, f32x16* snext, u32x4* pcur,
                        u32x4* pnext) __attribute__((always_inline)) {
     constexpr int jm = decltype(jm4_tag)::value;  // j % 4
@@ -447,19 +480,23 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     // wait for the loads still in flight (they target other stages); every
     // LDS read of the previous step has returned (lgkmcnt) before any wave
     // may overwrite its stage.  Loads of the previous step may stay in flight.
+    // Only the V loads of the previous step may stay in flight: its K loads
+    // (tile j+3) are read at the end of this step, for the next one.
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * NLD) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NLD) : "memory");
     __builtin_amdgcn_sched_barrier(0);
     issue_k(j + 4, kbuf(jm));
     issue_v(j + 2, vbuf((jm + 2) & 3));
     const char* kt = kbuf((jm + 2) & 3);
     const char* vt = vbuf(jm);
 
-    if (redo) reref(snext, pcur);  // (snext still holds the scores of tile j)
-    zero_scores(snext);
+    if (redo) reref(snext, pcur, scur);  // (snext still holds the scores of tile j)
     const float ts = tile_exp(scur, pnext, Flag<false>{});
+    // the first NPF K fragments of tile j+2 were read by the previous step
 #pragma unroll
-    for (int i = 0; i < NS; ++i) snext[i / DK] = mfma_32x32x16<BF16>(k_frag(kt, i), qf[i % DK], snext[i / DK]);
+    for (int i = 0; i < NS; ++i)
+      snext[i / DK] = mfma_32x32x16<BF16>(i < NPF ? kpre[i] : k_frag(kt, i), qf[i % DK],
+                                          i % DK == 0 ? negm : snext[i / DK]);
 #pragma unroll
     for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -478,6 +515,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
     }
+    // K fragments of tile j+3 for the next step
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) kpre[i] = k_frag(kbuf((jm + 3) & 3), i);
     // pin the packed P to this block: the packing would otherwise sink past
     // the next step's redo branch, out of the interleaved schedule
 #pragma unroll
@@ -496,12 +536,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     if (j < nt_w) {
       const char* kt = kbuf((j + 2) & 3);
       const char* vt = vbuf(j & 3);
-      if (redo) reref(snext, pcur);
-      if (j + 2 < nt_w) {
-        zero_scores(snext);
-#pragma unroll
-        for (int i = 0; i < NS; ++i) snext[i / DK] = mfma_32x32x16<BF16>(k_frag(kt, i), qf[i % DK], snext[i / DK]);
-      }
+      if (redo) reref(snext, pcur, scur);
+      if (j + 2 < nt_w) score_tile(snext, kt);
       float ts = 0.f;
       if (j + 1 < nt_w) {
         apply_mask(scur, (j + 1) * BN);
@@ -519,23 +555,31 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   // ---- prologue: scores of tiles 0 and 1, P of tile 0
   f32x16 sa[KB], sb[KB];
   u32x4 pa[NU], pb[NU];
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NLD) : "memory");  // K 0 and K 1 have landed
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NLD) : "memory");  // K 0, K 1 and K 2 have landed
   __syncthreads();
   if (nt_w > 0) {
-    zero_scores(sa);
-    zero_scores(sb);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) sa[i / DK] = mfma_32x32x16<BF16>(k_frag(kbuf(0), i), qf[i % DK], sa[i / DK]);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) sb[i / DK] = mfma_32x32x16<BF16>(k_frag(kbuf(1), i), qf[i % DK], sb[i / DK]);
-    // (every row's first maximum is finite: key 0 is never masked)
+    // tile 0 from a zero reference; its row maximum becomes the reference
+    // (finite: key 0 is never masked)
+    set_negm();
+    score_tile(sa, kbuf(0));
     apply_mask(sa, 0);
-    reref(sa, pa);
+    m_ref = tile_max(sa);
+    set_negm();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sa[kb][r] -= m_ref;
+    l_run = tile_exp(sa, pa, Flag<true>{});
+    score_tile(sb, kbuf(1));
   }
 
   // step j: scores of tile j+1 in sb (j even) or sa (j odd), P of tile j in
   // pa (j even) or pb (j odd)
   int j = 0;
+  if (j_fast > 0) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) kpre[i] = k_frag(kbuf(2), i);
+  }
   for (; j < j_fast; j += 4) {
     step_fast(j, Int<0>{}, sb, sa, pa, pb);
     step_fast(j + 1, Int<1>{}, sa, sb, pb, pa);
@@ -586,7 +630,7 @@ hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream
   p.n_qblk = (int)((Sq + kBM - 1) / kBM);
   p.n_wg = (int)(BH * p.n_qblk);
   void* args[] = {&p};
-  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN>);
+  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN, false>);
   return hipLaunchKernel(fn, dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
 }
 
@@ -634,6 +678,7 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
   p.n_wg = 0;
   p.c = (float)(fabs((double)scale) * 1.4426950408889634);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
+  p.cs = (float)((double)scale * 1.4426950408889634);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = dtype == FA_BF16;
