@@ -100,7 +100,6 @@ struct Params {
   int n_wg;        // total work-groups
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 when scale < 0 (q is negated on load), else 0
-  float cs;        // scale * log2(e), by which q is multiplied on load when pre-scaling
 };
 
 template <bool BF16>
@@ -211,10 +210,7 @@ struct Flag { static constexpr bool value = B; };
 template <int I>
 struct Int { static constexpr int value = I; };
 
-// PRE (fp16 only): q is multiplied by scale*log2(e) (rounded to fp16) as it
-// is loaded, so the score products give exp2-domain logits and P = exp2(s)
-// needs no instruction besides the exponential.
-template <int D, bool BF16, bool CAUSAL, int BN, bool PRE>
+template <int D, bool BF16, bool CAUSAL, int BN>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                     // bytes per row
@@ -227,7 +223,6 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int NS = KB * DK;                     // score products per tile
   constexpr int NSA = NS / 2;                     // of which issued ahead of the row maximum
   static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over the waves");
-  static_assert(!(PRE && BF16), "pre-scaling rounds q to fp16");
   static_assert(DK >= NSA, "the early score products must share one 32-key block");
 
   // A ring of four LDS stages per tensor (tile t in stage t % 4), each a
@@ -315,14 +310,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int ks = 0; ks < DK; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (qi < p.Sq) x = *reinterpret_cast<const u32x4*>(qg + (size_t)qi * D + ks * 16 + h * 8);
-    if constexpr (PRE) {
-      f16x8 v = __builtin_bit_cast(f16x8, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (_Float16)((float)v[e] * p.cs);
-      x = __builtin_bit_cast(u32x4, v);
-    } else {
-      x ^= p.qsign;
-    }
+    x ^= p.qsign;
     qf[ks] = x;
   }
 
@@ -350,13 +338,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  // The scores in registers are relative to a per-row reference m_ref
-  // (score units: raw, or exp2 units when PRE): every score product starts
-  // from negm = -m_ref in all 16 accumulator slots instead of from 0, so
-  // the subtraction costs no instruction.
+  // The scores in registers are relative to a per-row reference m_ref (in
+  // raw score units): every score product starts from negm = -m_ref in all
+  // 16 accumulator slots instead of from 0, so the subtraction costs no
+  // instruction.
   float m_ref = 0.f;
   float l_run = 0.f;        // this half's share of the running normaliser
-  const float c = PRE ? 1.f : p.c;  // score -> exp2 units
+  const float c = p.c;      // raw score -> exp2 units
   f32x16 negm;
   auto set_negm = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -409,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
   };
 
-  // P = exp2(s*c) of the relative scores (PRE: exp2(s)), packed to 16 bits
+  // P = exp2(s*c) of the relative scores, packed to 16 bits
   // into pout; returns this lane's sum of the tile's P (fp32: v_add_f32 runs
   // beside the matrix instructions, a v_dot2 of the packed values would not).
   auto tile_exp = [&](const f32x16* sacc, u32x4* pout, auto mask_tag) __attribute__((always_inline)) -> float {
@@ -421,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         const float sv = sacc[u >> 1][8 * (u & 1) + t8];
-        float pe = __builtin_amdgcn_exp2f(PRE ? sv : sv * c);
+        float pe = __builtin_amdgcn_exp2f(sv * c);
         if constexpr (MASK) pe = (sv == -INFINITY) ? 0.f : pe;  // also covers scale == 0
         pv[t8] = pe;
       }
@@ -630,7 +618,7 @@ hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream
   p.n_qblk = (int)((Sq + kBM - 1) / kBM);
   p.n_wg = (int)(BH * p.n_qblk);
   void* args[] = {&p};
-  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN, false>);
+  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN>);
   return hipLaunchKernel(fn, dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
 }
 
@@ -678,7 +666,6 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
   p.n_wg = 0;
   p.c = (float)(fabs((double)scale) * 1.4426950408889634);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
-  p.cs = (float)((double)scale * 1.4426950408889634);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = dtype == FA_BF16;
