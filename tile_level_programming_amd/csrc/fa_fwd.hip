@@ -402,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   // beside the matrix instructions, a v_dot2 of the packed values would not).
   auto tile_exp = [&](const f32x16* sacc, u32x4* pout, auto mask_tag) __attribute__((always_inline)) -> float {
     constexpr bool MASK = decltype(mask_tag)::value;
-    float ps[2] = {0.f, 0.f};
+    float ps[2];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       float pv[8];
@@ -416,7 +416,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pout[u][e] = pack2<BF16>(pv[2 * e], pv[2 * e + 1]);
-        ps[e & 1] += pv[2 * e] + pv[2 * e + 1];
+        const float pair = pv[2 * e] + pv[2 * e + 1];
+        ps[e & 1] = (u == 0 && e < 2) ? pair : ps[e & 1] + pair;
       }
     }
     return ps[0] + ps[1];
@@ -463,15 +464,15 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   auto step_fast = [&](int j, auto jm4_tag, f32x16* scur, f32x16* snext, u32x4* pcur,
                        u32x4* pnext) __attribute__((always_inline)) {
     constexpr int jm = decltype(jm4_tag)::value;  // j % 4
-    // the wait and the barrier in one asm statement with a memory clobber:
+    // The wait and the barrier in one asm statement with a memory clobber:
     // no LDS access moves across it, and no release fence makes the compiler
-    // wait for the loads still in flight (they target other stages); every
-    // LDS read of the previous step has returned (lgkmcnt) before any wave
-    // may overwrite its stage.  Loads of the previous step may stay in flight.
-    // Only the V loads of the previous step may stay in flight: its K loads
-    // (tile j+3) are read at the end of this step, for the next one.
+    // wait for the loads still in flight (they target other stages).  Only
+    // the V loads of the previous step may stay in flight: its K loads (tile
+    // j+3) are read at the end of this step, for the next one.  LDS reads
+    // need not have returned: the stages this step overwrites (K tile j, V
+    // tile j-2) were last read, and their fragments used, two steps ago.
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NLD) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NLD) : "memory");
     __builtin_amdgcn_sched_barrier(0);
     issue_k(j + 4, kbuf(jm));
     issue_v(j + 2, vbuf((jm + 2) & 3));
