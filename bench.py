@@ -45,8 +45,14 @@ def log(*a):
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source with // comments and blank lines removed:
+    counters taken on a source stay valid across comment edits, not code edits."""
+    import re
+
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        lines = [re.sub(r"\s*//.*$", "", ln).rstrip() for ln in f]
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_for(workload: str):

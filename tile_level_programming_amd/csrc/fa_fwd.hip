@@ -29,12 +29,12 @@
 //    i/4, i/4+4, i/4+8, i/4+12 point at).  The key order of a product's K
 //    slots is free; the read addresses follow the order in which the
 //    accumulator layout holds P.
-//  * Software pipeline across key tiles: while the vector unit exponentiates
-//    tile j, the matrix unit computes the scores of tile j+1 and the P.V
-//    product of tile j, with the instructions interleaved so one wave keeps
-//    both units busy.  K therefore runs one tile ahead of V in LDS: at tile j
-//    the K tile j+1 and the V tile j are resident while K j+2 and V j+1
-//    stream in.
+//  * Software pipeline across key tiles, three deep: step j runs the score
+//    products of tile j+2 and the P.V product of tile j on the matrix unit,
+//    interleaved with the exponentials of tile j+1 on the vector unit; the
+//    two streams share no data.  K tiles run two ahead of V in LDS, in a
+//    ring of four stages per tensor, and the K fragments of a step are read
+//    from LDS by the step before.
 //  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 with
 //    LDS destination: lane l of an instruction fills bytes 16l..16l+15 of a
 //    1 KB block).  Each lane picks which 16-byte chunk of the tile it fetches,
@@ -43,12 +43,14 @@
 //    banks, V rows so that the transposing reads of 4 consecutive rows hit
 //    distinct banks.  The buffer's range ends at the last key, so rows past
 //    the end of the keys arrive as zeros.
-//  * Online softmax with exp2 and scale*log2(e) folded into one FMA per
-//    score.  Rescaling is lazy: a wave moves its reference maxima (and
-//    rescales O and the sums) only when some row's maximum has grown by more
-//    than 2^8 in exp2 units; otherwise the exponentials are taken against the
-//    old reference and stay below 2^8, which 16-bit P holds at full relative
-//    precision.  The reference cancels in O and is carried into lse.
+//  * Online softmax with exp2 (scale*log2(e) applied as one multiply per
+//    score) against a per-row reference m.  The score products start from
+//    -m, so the scores come out relative to it at no cost.  The reference
+//    is the first tile's row maximum and moves only when a tile's P grows
+//    large (a lane's sum over the tile above a bound): then O and the sums
+//    are rescaled and the tile is exponentiated again.  No per-tile row
+//    maximum is taken otherwise.  The reference cancels in O and is carried
+//    into lse.
 //  * Tiles that need no mask run a branch-free path; tiles that cross the
 //    causal diagonal or the end of the keys take the masked path; causal tiles
 //    wholly above a wave's queries are skipped by that wave and never loaded
