@@ -201,6 +201,30 @@ def test_rising_logits(torch_dev, fa, oracle_mod, D, dtype, causal):
     full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(D), causal, f"rising {D} {dtype}")
 
 
+@pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_nan_query_rows_stay_in_their_rows(torch_dev, fa, oracle_mod, D, dtype, causal):
+    # A NaN in a query row makes that row's scores, O and lse NaN and must
+    # leave every other row exact.  Rows 16 and 140 pair with rows 0 and 124
+    # in the matrix-unit row sums (query n and n+16 of a wave share a column
+    # there), rows 5 and 21 are such a pair both poisoned.
+    torch = torch_dev
+    Sq, Sk = 300, 1500
+    q = fi.tensor_bits(26, "q", (1, 2, Sq, D), dtype)
+    k = fi.tensor_bits(26, "k", (1, 2, Sk, D), dtype)
+    v = fi.tensor_bits(26, "v", (1, 2, Sk, D), dtype)
+    bad = [5, 16, 21, 140]
+    qn = q.copy()
+    qn[0, 0, bad, 3] = 0x7E00 if dtype == "f16" else 0x7FC0
+    o, lse = run_gpu(torch, fa, qn, k, v, dtype, 1.0 / math.sqrt(D), causal)
+    o, lse = to_f64(torch, o), lse.double().cpu().numpy()
+    assert np.all(np.isnan(o[0, 0, bad])) and np.all(np.isnan(lse[0, 0, bad]))
+    good = np.ones((1, 2, Sq), bool)
+    good[0, 0, bad] = False
+    o_ref, lse_ref = oracle_mod.attention(q, k, v, dtype, 1.0 / math.sqrt(D), causal, threads=THREADS)
+    check(o[good], lse[good], o_ref[good], lse_ref[good], dtype, f"nan rows {D} {dtype}")
+
+
 # --- properties checkable without the oracle ---------------------------------
 
 

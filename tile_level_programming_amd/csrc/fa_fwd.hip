@@ -47,10 +47,12 @@
 //    score) against a per-row reference m.  The score products start from
 //    -m, so the scores come out relative to it at no cost.  The reference
 //    is the first tile's row maximum and moves only when a tile's P grows
-//    large (a lane's sum over the tile above a bound): then O and the sums
+//    large (a row's sum over the tile above a bound): then O and the sums
 //    are rescaled and the tile is exponentiated again.  No per-tile row
 //    maximum is taken otherwise.  The reference cancels in O and is carried
-//    into lse.
+//    into lse.  The branch-free steps take the row sums of the packed P on
+//    the matrix unit (a 0/1 operand), which keeps 32 additions per lane and
+//    tile off the vector unit.
 //  * Tiles that need no mask run a branch-free path; tiles that cross the
 //    causal diagonal or the end of the keys take the masked path; causal tiles
 //    wholly above a wave's queries are skipped by that wave and never loaded
@@ -72,13 +74,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLn2 = 0.6931471805599453f;
-// A lane's sum of P over one tile above this makes its wave move the
+// A row's sum of P over one tile above this makes its wave move the
 // reference (and rescale); below it every P of the tile is at most this,
 // far inside the 16-bit range (fp16 max 65504).
 constexpr float kSumBound = 4096.0f;
@@ -111,6 +114,16 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 acc) {
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 acc) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
 }
 
@@ -345,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   // 16 accumulator slots instead of from 0, so the subtraction costs no
   // instruction.
   float m_ref = 0.f;
-  float l_run = 0.f;        // this half's share of the running normaliser
+  float l_run = 0.f;        // running normaliser of this lane's query (both halves hold it)
   const float c = p.c;      // raw score -> exp2 units
   f32x16 negm;
   auto set_negm = [&]() __attribute__((always_inline)) {
@@ -400,8 +413,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   };
 
   // P = exp2(s*c) of the relative scores, packed to 16 bits
-  // into pout; returns this lane's sum of the tile's P (fp32: v_add_f32 runs
-  // beside the matrix instructions, a v_dot2 of the packed values would not).
+  // into pout; returns this lane's sum of the tile's P in fp32 (half of the
+  // tile's keys: sum_halves gives the row's).  The branch-free steps ignore
+  // it and take the row sums on the matrix unit (tile_sum).
   auto tile_exp = [&](const f32x16* sacc, u32x4* pout, auto mask_tag) __attribute__((always_inline)) -> float {
     constexpr bool MASK = decltype(mask_tag)::value;
     float ps[2];
@@ -425,6 +439,32 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     return ps[0] + ps[1];
   };
 
+  // Row sums of a tile's packed P on the matrix unit: four 16x16x32
+  // products with a constant 0/1 A operand.  Read as a 16x16x32 B operand,
+  // the P registers of lane l hold column l%16 and k rows 8(l/16)..+7, that
+  // is 8 keys of query l%16 (l/16 even) or of query l%16+16 (l/16 odd),
+  // lanes l and l+32 covering the 16 keys of a slice.  A row m of ones over
+  // the k blocks of one query puts that query's sum in output row m; rows
+  // 0, 8 take queries 0..15 and rows 4, 12 queries 16..31, and output
+  // register 0 of lane l is row 4(l/16) of column l%16: the sum of the
+  // lane's own query, in both halves of the wave.  Every other output row
+  // is zero.  A row's sum also multiplies the other query of its column by
+  // zero, so an inf or NaN P of that query makes it NaN; the steps treat a
+  // NaN sum like one above the bound and take the rows' sums again, in
+  // fp32 on the vector unit.
+  const u32x4 ones = [&]() {
+    const uint32_t one2 = BF16 ? 0x3f803f80u : 0x3c003c00u;
+    const int m = lane & 15, gk = lane >> 4;
+    const uint32_t x = ((m & 3) == 0 && ((m >> 2) & 1) == (gk & 1)) ? one2 : 0u;
+    return u32x4{x, x, x, x};
+  }();
+  auto tile_sum = [&](const u32x4* pt) __attribute__((always_inline)) -> float {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc = mfma_16x16x32<BF16>(ones, pt[u], acc);
+    return acc[0];
+  };
+
   // The reference moves up to the row's running maximum when some lane's
   // sum over a tile exceeded kSumBound (then its P are no longer known to be
   // small).  st: that tile's scores, exponentiated again into pout; snx: the
@@ -444,7 +484,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
       }
     const float alpha = exp2f(-delta * c);
     scale_o(alpha);
-    l_run = l_run * alpha + tile_exp(st, pout, Flag<true>{});
+    l_run = l_run * alpha + sum_halves(tile_exp(st, pout, Flag<true>{}));
   };
   // set by a step whose exponentials hit the bound: the next step, before
   // its products, re-references that tile (its scores are still in the
@@ -482,7 +522,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     const char* vt = vbuf(jm);
 
     if (redo) reref(snext, pcur, scur);  // (snext still holds the scores of tile j)
-    const float ts = tile_exp(scur, pnext, Flag<false>{});
+    tile_exp(scur, pnext, Flag<false>{});
     // the first NPF K fragments of tile j+2 were read by the previous step
 #pragma unroll
     for (int i = 0; i < NS; ++i)
@@ -492,12 +532,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] = mfma_32x32x16<BF16>(v_frag(vt, u, db), pcur[u], oacc[db]);
+    const float ts = tile_sum(pnext);
     {
-      // one matrix instruction, then a run of vector instructions and two
-      // LDS reads (the first K fragments are read up front)
-      constexpr int NMF = NS + NU * DB;
-      constexpr int NV = NU * (8 + 8 + 4 + 8);
-      constexpr int VPM = (NV + NMF - 1) / NMF;
+      // one matrix instruction, then up to three vector instructions and two
+      // LDS reads (the first K fragments are read up front); the vector
+      // work (per 16-key slice 8 multiplies, 8 exponentials and 4 packs)
+      // is spread over most of the step
+      constexpr int NMF = NS + NU * DB + NU;
+      constexpr int VPM = 3;
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
       for (int i = 0; i < NMF; ++i) {
@@ -513,7 +555,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     // the next step's redo branch, out of the interleaved schedule
 #pragma unroll
     for (int u = 0; u < NU; ++u) asm volatile("" ::"v"(pnext[u]));
-    redo = __builtin_amdgcn_ballot_w64(ts > kSumBound) != 0;
+    redo = __builtin_amdgcn_ballot_w64(!(ts <= kSumBound)) != 0;
     if (!redo) l_run += ts;
   };
 
@@ -532,7 +574,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
       float ts = 0.f;
       if (j + 1 < nt_w) {
         apply_mask(scur, (j + 1) * BN);
-        ts = tile_exp(scur, pnext, Flag<true>{});
+        ts = sum_halves(tile_exp(scur, pnext, Flag<true>{}));
       }
 #pragma unroll
       for (int u = 0; u < NU; ++u)
@@ -560,7 +602,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sa[kb][r] -= m_ref;
-    l_run = tile_exp(sa, pa, Flag<true>{});
+    l_run = sum_halves(tile_exp(sa, pa, Flag<true>{}));
     score_tile(sb, kbuf(1));
   }
 
@@ -589,7 +631,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
 
   // ---- epilogue: normalise, round, store O rows and lse
   if (qw0 < p.Sq) {
-    const float l = sum_halves(l_run);
+    const float l = l_run;
     if (qi < p.Sq) {
       const float inv = 1.f / l;
       uint16_t* og = p.o + ((size_t)bh * p.Sq + qi) * D;
