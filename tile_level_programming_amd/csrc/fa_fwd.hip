@@ -516,6 +516,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NLD) : "memory");
     __builtin_amdgcn_sched_barrier(0);
+    // the step's products and exponentials run at raised issue priority;
+    // the row-sum check and the wait at the next barrier run at the normal
+    // one, so a SIMD's other wave, in the middle of its step, issues first
+    // (measured: +0.5%)
+    __builtin_amdgcn_s_setprio(1);
     issue_k(j + 4, kbuf(jm));
     issue_v(j + 2, vbuf((jm + 2) & 3));
     const char* kt = kbuf((jm + 2) & 3);
@@ -555,6 +560,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     // the next step's redo branch, out of the interleaved schedule
 #pragma unroll
     for (int u = 0; u < NU; ++u) asm volatile("" ::"v"(pnext[u]));
+    __builtin_amdgcn_s_setprio(0);
     redo = __builtin_amdgcn_ballot_w64(!(ts <= kSumBound)) != 0;
     if (!redo) l_run += ts;
   };
