@@ -57,6 +57,15 @@ def _load():
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_double, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.fa_oracle_rows_range.restype = ctypes.c_int
+        lib.fa_oracle_rows_range.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+                                             ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.fa_oracle_merge.restype = ctypes.c_int
+        lib.fa_oracle_merge.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.fa_oracle_init()
         _lib = lib
         return lib
@@ -71,11 +80,14 @@ def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
     return out
 
 
-def attention_rows(q, k, v, dtype: str, scale: float, causal: bool, rows=None, threads: int = 1):
+def attention_rows(q, k, v, dtype: str, scale: float, causal: bool, rows=None, threads: int = 1,
+                   key_range=None):
     """Oracle O rows and lse for flat query rows ``rows`` (all rows if None).
 
     q: uint16 [B,H,Sq,D]; k, v: uint16 [B,H,Sk,D].  Returns (o [n, D] float64,
-    lse [n] float64) for the requested rows, in the order given.
+    lse [n] float64) for the requested rows, in the order given.  With
+    ``key_range=(a, b)`` only keys a <= j < b take part (causal mask on the
+    global key index); rows that see none of them get lse -inf and o 0.
     """
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.uint16)
@@ -92,13 +104,22 @@ def attention_rows(q, k, v, dtype: str, scale: float, causal: bool, rows=None, t
     o = np.empty((n, D), dtype=np.float64)
     lse = np.empty(n, dtype=np.float64)
 
+    k0, k1 = (0, Sk) if key_range is None else (int(key_range[0]), int(key_range[1]))
+    if not 0 <= k0 < k1 <= Sk:
+        raise ValueError("key_range must satisfy 0 <= a < b <= Sk")
+
     def run(a, b):
         if b <= a:
             return 0
-        return lib.fa_oracle_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, DTYPE_CODE[dtype],
-                                  B, H, Sq, Sk, D, float(scale), int(bool(causal)),
-                                  rows[a:].ctypes.data, b - a,
-                                  o[a:].ctypes.data, lse[a:].ctypes.data)
+        if key_range is None:
+            return lib.fa_oracle_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, DTYPE_CODE[dtype],
+                                      B, H, Sq, Sk, D, float(scale), int(bool(causal)),
+                                      rows[a:].ctypes.data, b - a,
+                                      o[a:].ctypes.data, lse[a:].ctypes.data)
+        return lib.fa_oracle_rows_range(q.ctypes.data, k.ctypes.data, v.ctypes.data, DTYPE_CODE[dtype],
+                                        B, H, Sq, Sk, D, float(scale), int(bool(causal)), k0, k1,
+                                        rows[a:].ctypes.data, b - a,
+                                        o[a:].ctypes.data, lse[a:].ctypes.data)
 
     threads = max(1, int(threads))
     if threads == 1 or n < 2 * threads:
@@ -121,3 +142,26 @@ def attention(q, k, v, dtype: str, scale: float, causal: bool, threads: int = 1)
     B, H, Sq, D = q.shape
     o, lse = attention_rows(q, k, v, dtype, scale, causal, None, threads)
     return o.reshape(B, H, Sq, D), lse.reshape(B, H, Sq)
+
+
+def merge(o_parts, lse_parts):
+    """Log-sum-exp merge of partial results over disjoint key ranges.
+
+    o_parts: float64 [G, ..., D]; lse_parts: float64 [G, ...] (the same
+    leading shape).  Returns (o [..., D], lse [...]), see fa_oracle_merge.
+    """
+    lib = _load()
+    o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    G, D = o_parts.shape[0], o_parts.shape[-1]
+    lead = lse_parts.shape[1:]
+    if o_parts.shape != (G, *lead, D) or lse_parts.shape[0] != G:
+        raise ValueError("o_parts must be [G, ..., D] and lse_parts [G, ...] with the same leading shape")
+    nrows = int(np.prod(lead, dtype=np.int64))
+    o = np.empty((nrows, D), dtype=np.float64)
+    lse = np.empty(nrows, dtype=np.float64)
+    rc = lib.fa_oracle_merge(G, nrows, D, o_parts.ctypes.data, lse_parts.ctypes.data,
+                             o.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("fa_oracle_merge failed")
+    return o.reshape(*lead, D), lse.reshape(lead)

@@ -29,6 +29,10 @@
  * is the natural log of the normalising sum of the scaled logits, and the
  * layout is contiguous [B, H, S, D] with D fastest.
  *
+ * Two more routines serve a split over the keys: fa_oracle_rows_range (the
+ * same rows over a key range) and fa_oracle_merge (the log-sum-exp merge of
+ * partial results; see there).
+ *
  * Inputs are fp16 or bf16 bit patterns (uint16); they are decoded exactly to
  * double.  All arithmetic is double, in the order written above, one row at
  * a time, with no tiling or online rescaling.  Rows are independent, so a
@@ -91,15 +95,23 @@ void fa_oracle_decode(const uint16_t* bits, int64_t n, int dtype, double* out) {
 }
 
 /*
- * Evaluate rows rows[0..nrows-1] (flat row index (b*H + h)*Sq + i).
+ * Evaluate rows rows[0..nrows-1] (flat row index (b*H + h)*Sq + i) over the
+ * keys k_begin <= j < k_end only (0 <= k_begin < k_end <= Sk); the causal mask
+ * uses the global key index j.  This is the same row computation with the
+ * other keys left out, as when the keys of a row are split into ranges.  A
+ * row that sees no key of the range (causal, i < k_begin) has an empty
+ * softmax: its lse is -inf and its o is 0, which gives it zero weight in
+ * fa_oracle_merge.
  * q: [B,H,Sq,D]; k, v: [B,H,Sk,D] bit patterns.  o: [nrows, D] doubles,
  * lse: [nrows] doubles.  Returns 0, or -1 on bad arguments / no memory.
  */
-int fa_oracle_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
-                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                   double scale, int causal,
-                   const int64_t* rows, int64_t nrows, double* o, double* lse) {
+int fa_oracle_rows_range(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
+                         int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                         double scale, int causal, int64_t k_begin, int64_t k_end,
+                         const int64_t* rows, int64_t nrows, double* o, double* lse) {
     if (!g_ready || (dtype != 0 && dtype != 1) || B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1)
+        return -1;
+    if (k_begin < 0 || k_end > Sk || k_begin >= k_end)
         return -1;
     const double* tab = g_tab[dtype];
     double* qd = (double*)malloc(sizeof(double) * (size_t)D);
@@ -121,7 +133,7 @@ int fa_oracle_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int 
         for (int64_t d = 0; d < D; ++d) qd[d] = tab[qrow[d]];
 
         /* scores, explicit, with the mask applied after scaling */
-        for (int64_t j = 0; j < Sk; ++j) {
+        for (int64_t j = k_begin; j < k_end; ++j) {
             if (causal && j > i) {
                 s[j] = -INFINITY;
                 continue;
@@ -133,17 +145,22 @@ int fa_oracle_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int 
 
         /* softmax */
         double m = -INFINITY;
-        for (int64_t j = 0; j < Sk; ++j)
+        for (int64_t j = k_begin; j < k_end; ++j)
             if (s[j] > m) m = s[j];
+        if (m == -INFINITY) {       /* no visible key in the range: empty softmax */
+            for (int64_t d = 0; d < D; ++d) o[r * D + d] = 0.0;
+            lse[r] = -INFINITY;
+            continue;
+        }
         double l = 0.0;
-        for (int64_t j = 0; j < Sk; ++j) {
+        for (int64_t j = k_begin; j < k_end; ++j) {
             s[j] = exp(s[j] - m);   /* s now holds p_j; exp(-inf) = 0 */
             l += s[j];
         }
 
         /* output */
         for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
-        for (int64_t j = 0; j < Sk; ++j) {
+        for (int64_t j = k_begin; j < k_end; ++j) {
             double p = s[j];
             for (int64_t d = 0; d < D; ++d) acc[d] += p * tab[vh[j * D + d]];
         }
@@ -151,5 +168,51 @@ int fa_oracle_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int 
         lse[r] = m + log(l);
     }
     free(qd); free(s); free(acc);
+    return 0;
+}
+
+/* All Sk keys: the definition in the header comment. */
+int fa_oracle_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
+                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                   double scale, int causal,
+                   const int64_t* rows, int64_t nrows, double* o, double* lse) {
+    return fa_oracle_rows_range(q, k, v, dtype, B, H, Sq, Sk, D, scale, causal, 0, Sk,
+                                rows, nrows, o, lse);
+}
+
+/*
+ * Merge of partial results over disjoint key ranges that together cover a
+ * row's keys.  The pages' online softmax combines the running result of the
+ * keys seen so far with a new tile's by rescaling both to a common maximum;
+ * two finished partial results combine the same way.  With part g holding
+ * o_g (normalised over its keys) and lse_g = m_g + ln l_g, for each row:
+ *   M   = max_g lse_g
+ *   lse = M + ln( sum_g exp(lse_g - M) )
+ *   o   = sum_g exp(lse_g - lse) * o_g
+ * Parts with lse_g = -inf (empty ranges) get zero weight; a row whose parts
+ * are all empty gets lse = -inf and o = 0.
+ * o_parts: [n_part][nrows][D], lse_parts: [n_part][nrows]; o: [nrows][D],
+ * lse: [nrows].  Returns 0, or -1 on bad arguments.
+ */
+int fa_oracle_merge(int64_t n_part, int64_t nrows, int64_t D, const double* o_parts,
+                    const double* lse_parts, double* o, double* lse) {
+    if (n_part < 1 || nrows < 0 || D < 1) return -1;
+    for (int64_t r = 0; r < nrows; ++r) {
+        double M = -INFINITY;
+        for (int64_t g = 0; g < n_part; ++g)
+            if (lse_parts[g * nrows + r] > M) M = lse_parts[g * nrows + r];
+        for (int64_t d = 0; d < D; ++d) o[r * D + d] = 0.0;
+        if (M == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double sum = 0.0;
+        for (int64_t g = 0; g < n_part; ++g) sum += exp(lse_parts[g * nrows + r] - M);
+        lse[r] = M + log(sum);
+        for (int64_t g = 0; g < n_part; ++g) {
+            double w = exp(lse_parts[g * nrows + r] - lse[r]);
+            for (int64_t d = 0; d < D; ++d) o[r * D + d] += w * o_parts[(g * nrows + r) * D + d];
+        }
+    }
     return 0;
 }

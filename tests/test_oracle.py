@@ -281,3 +281,92 @@ def test_rows_subset_and_threads(oracle_mod):
     ot, lt = oracle_mod.attention(q, k, v, w.dtype, w.scale, True, threads=7)
     np.testing.assert_array_equal(ot, o)
     np.testing.assert_array_equal(lt, lse)
+
+
+# --- split over the keys: key ranges and the log-sum-exp merge --------------
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_range_is_attention_over_sliced_keys(oracle_mod, causal):
+    # keys a <= j < b only: for non-causal rows, and for causal rows that see
+    # the whole range (i >= b-1), the same as the oracle on the sliced k and
+    # v; a causal row a <= i < b-1 sees keys a..i; rows i < a see nothing
+    dtype = "f16"
+    B, H, Sq, Sk, D = 1, 2, 48, 40, 16
+    q = _rand((B, H, Sq, D), dtype, 31)
+    k = fi.tensor_bits(31, "k", (B, H, Sk, D), dtype)
+    v = fi.tensor_bits(31, "v", (B, H, Sk, D), dtype)
+    a, b = 9, 27
+    o, lse = oracle_mod.attention_rows(q, k, v, dtype, 0.4, causal, key_range=(a, b))
+    o, lse = o.reshape(B, H, Sq, D), lse.reshape(B, H, Sq)
+    ks, vs = np.ascontiguousarray(k[:, :, a:b]), np.ascontiguousarray(v[:, :, a:b])
+    os_, ls_ = oracle_mod.attention(q, ks, vs, dtype, 0.4, False)
+    for i in range(Sq):
+        if not causal or i >= b - 1:
+            np.testing.assert_allclose(o[:, :, i], os_[:, :, i], rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(lse[:, :, i], ls_[:, :, i], rtol=1e-14)
+        elif i >= a:
+            n = i - a + 1
+            oi, li = oracle_mod.attention(np.ascontiguousarray(q[:, :, i:i + 1]), np.ascontiguousarray(ks[:, :, :n]),
+                                          np.ascontiguousarray(vs[:, :, :n]), dtype, 0.4, False)
+            np.testing.assert_allclose(o[:, :, i], oi[:, :, 0], rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(lse[:, :, i], li[:, :, 0], rtol=1e-14)
+        else:
+            assert np.all(lse[:, :, i] == -np.inf) and np.all(o[:, :, i] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cuts", [(0, 100), (0, 37, 100), (0, 5, 64, 65, 100), (0, 1, 2, 3, 100)])
+def test_merge_of_key_ranges_is_full_attention(oracle_mod, causal, cuts):
+    # the log-sum-exp merge of partials over disjoint key ranges that cover
+    # all keys gives the unsplit result (causal: rows below a range's start
+    # contribute empty parts)
+    dtype = "bf16"
+    B, H, Sq, Sk, D = 2, 1, 100, 100, 8
+    q = _rand((B, H, Sq, D), dtype, 32, 2.0)
+    k = fi.tensor_bits(32, "k", (B, H, Sk, D), dtype, 2.0)
+    v = fi.tensor_bits(32, "v", (B, H, Sk, D), dtype)
+    parts = [oracle_mod.attention_rows(q, k, v, dtype, 0.35, causal, key_range=(a, b))
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    o, lse = oracle_mod.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    of, lf = oracle_mod.attention(q, k, v, dtype, 0.35, causal)
+    np.testing.assert_allclose(o.reshape(of.shape), of, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse.reshape(lf.shape), lf, rtol=1e-13, atol=1e-13)
+
+
+def test_merge_closed_forms(oracle_mod):
+    D = 3
+    o1 = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0], [7.0, 8.0, 9.0], [1.0, 1.0, 1.0]])
+    o2 = np.array([[3.0, 2.0, 1.0], [0.0, 0.0, 0.0], [-1.0, 0.0, 1.0], [2.0, 2.0, 2.0]])
+    l1 = np.array([0.5, 2.0, -np.inf, -np.inf])
+    l2 = np.array([0.5, -np.inf, 1.0, -np.inf])
+    o2[1] = 0.0
+    o1[2] = o1[2] * 0  # empty parts hold o = 0
+    o1[3] = o2[3] = 0.0
+    o, lse = oracle_mod.merge(np.stack([o1, o2]), np.stack([l1, l2]))
+    # equal weights: the mean, lse + ln 2
+    np.testing.assert_allclose(o[0], [2.0, 2.0, 2.0], rtol=1e-15)
+    assert lse[0] == pytest.approx(0.5 + math.log(2.0), rel=1e-15)
+    # one empty part: the other passes through
+    np.testing.assert_allclose(o[1], o1[1], rtol=1e-15)
+    np.testing.assert_allclose(o[2], o2[2], rtol=1e-15)
+    assert lse[1] == 2.0 and lse[2] == 1.0
+    # all parts empty
+    assert lse[3] == -np.inf and np.all(o[3] == 0.0)
+    # weights e^{lse_g - lse}: lse 0 and ln 3 give weights 1/4 and 3/4
+    o, lse = oracle_mod.merge(np.array([[[4.0] * D], [[8.0] * D]]), np.array([[0.0], [math.log(3.0)]]))
+    np.testing.assert_allclose(o[0], [7.0] * D, rtol=1e-15)
+    assert lse[0] == pytest.approx(math.log(4.0), rel=1e-15)
+
+
+def test_merge_part_order_irrelevant(oracle_mod):
+    rng = np.random.default_rng(5)
+    G, R, D = 5, 7, 4
+    op = rng.normal(size=(G, R, D))
+    lp = rng.normal(size=(G, R)) * 10
+    lp[1, 3] = -np.inf
+    o, lse = oracle_mod.merge(op, lp)
+    perm = rng.permutation(G)
+    o2, lse2 = oracle_mod.merge(op[perm], lp[perm])
+    np.testing.assert_allclose(o2, o, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-14)
