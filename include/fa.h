@@ -22,6 +22,7 @@
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -76,6 +77,82 @@ typedef enum {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                  float scale, int causal, int dtype, void* stream);
+
+/*
+ * Split over the keys, for calls with few query blocks and many keys
+ * (decode-shaped: small Sq, long Sk), where one work-group per (batch, head,
+ * 128-query block) would leave most of the GPU idle.  The pages' online
+ * softmax carries a running result across key tiles and rescales it to each
+ * new maximum; here the keys of a row are cut into ranges, each range's
+ * partial result (O normalised over the range, and its lse) is computed by
+ * its own work-groups, and the partials are combined by the same rescaling
+ * to a common maximum:
+ *
+ *     lse = M + ln sum_g exp(lse_g - M),   M = max_g lse_g
+ *     O   = sum_g exp(lse_g - lse) O_g
+ *
+ * The result is the one fa_fwd computes, up to rounding.
+ */
+
+/*
+ * Number of key ranges fa_fwd_split uses for this shape: n_split ranges of
+ * equal length (a multiple of 64 keys, so possibly fewer ranges than asked),
+ * or, for n_split = 0, a count chosen from the shape (enough ranges for about
+ * 2048 work-groups, each range at least 256 keys).  0 on invalid sizes.
+ */
+int64_t fa_fwd_split_count(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t n_split);
+
+/*
+ * Bytes of device workspace fa_fwd_split needs for these arguments:
+ * count * B*H*Sq * (D + 1) * 4 (fp32 partial O and lse per range).
+ * 0 on invalid sizes.
+ */
+size_t fa_fwd_split_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                   int64_t n_split);
+
+/*
+ * fa_fwd_split -- enqueue the attention forward pass split over the keys:
+ * the partial-result kernel, then the merge (fa_lse_merge's kernel), both on
+ * `stream`.  Arguments as for fa_fwd, plus:
+ *
+ * n_split    ranges requested (>= 1), or 0 to let the library choose; see
+ *            fa_fwd_split_count.
+ * workspace  device pointer, 16-byte aligned, at least
+ *            fa_fwd_split_workspace_size(B, H, Sq, Sk, D, n_split) bytes,
+ *            owned by the caller and overlapping no other argument.  Once
+ *            the stream has run the call, it holds the partials that were
+ *            merged: O parts as fp32 [count][B*H*Sq][D] from the start, then
+ *            lse parts as fp32 [count][B*H*Sq] (a row that sees no key of a
+ *            range has O part 0 and lse part -inf).
+ * workspace_bytes  its size; a smaller size than needed is FA_ERR_INVALID_ARG.
+ *
+ * Errors, ownership and asynchrony as for fa_fwd; in addition
+ * B*H*ceil(Sq/128)*count must be below 2^31.  The library allocates nothing.
+ */
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                       float scale, int causal, int dtype, int64_t n_split,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_lse_merge -- enqueue the log-sum-exp merge of partial attention results
+ * over disjoint key ranges (formula above), for rows computed anywhere (for
+ * example key ranges held by different devices).
+ *
+ * o_parts    device pointer, fp32 [n_part][rows][D], 16-byte aligned: each
+ *            part's O, normalised over its keys (0 for an empty part).
+ * lse_parts  device pointer, fp32 [n_part][rows]: each part's lse (-inf for
+ *            an empty part).
+ * n_part >= 1, rows >= 1, D = 64 or 128.
+ * o          device pointer, [rows][D] of `dtype`, 16-byte aligned; written,
+ *            rounded to nearest even.
+ * lse        device pointer, fp32 [rows]; written.  A row whose parts are
+ *            all empty gets lse -inf and O 0.
+ * The outputs must not overlap the inputs.  Checks, errors and asynchrony
+ * as for fa_fwd; NaN parts propagate.
+ */
+fa_status fa_lse_merge(const float* o_parts, const float* lse_parts, int64_t n_part, int64_t rows,
+                       int64_t D, void* o, float* lse, int dtype, void* stream);
 
 /* Static, never-NULL description of a status code (unknown codes included). */
 const char* fa_status_string(int status);

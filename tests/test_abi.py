@@ -29,7 +29,8 @@ def fa():
 
 
 def test_header_declares_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_status_string"]
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_split", "fa_fwd_split_count", "fa_fwd_split_workspace_size",
+                                     "fa_lse_merge", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -80,3 +81,84 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         mod._load()
+
+
+# --- split over the keys and the merge: host-side plan and checks ------------
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,n_req,want", [
+    (1, 1, 1, 64, 0, 1),          # too few keys to split
+    (1, 1, 1, 1000, 1, 1),
+    (1, 1, 1, 1000, 4, 4),        # chunk 256
+    (1, 1, 1, 1000, 3, 3),        # chunk 384: 384, 384, 232
+    (1, 1, 1, 100, 7, 2),         # at most one range per 64 keys: chunk 64
+    (2, 32, 1, 16384, 0, 32),     # auto: 2048 / 64 work-groups
+    (2, 32, 1, 4096, 0, 16),      # auto, capped at Sk / 256
+    (2, 32, 8192, 8192, 0, 1),    # 4096 work-groups already
+    (1, 4, 300, 65536, 0, 171),   # auto 2048/12 = 171 ranges of 384 keys
+])
+def test_split_count(fa, B, H, Sq, Sk, n_req, want):
+    n = fa.split_count(B, H, Sq, Sk, n_req)
+    assert n == want
+    chunk = -(-Sk // n)
+    assert n * chunk >= Sk
+    for D in (64, 128):
+        assert fa.split_workspace_size(B, H, Sq, Sk, D, n_req) == n * B * H * Sq * (D + 1) * 4
+
+
+def test_split_count_invalid(fa):
+    assert fa.split_count(0, 1, 1, 100, 0) == 0
+    assert fa.split_count(1, 1, 1, 100, -1) == 0
+    assert fa.split_workspace_size(1, 1, 1, 0, 64, 0) == 0
+
+
+W = 64 * A  # fake workspace address
+
+
+def _call_split(fa, **kw):
+    args = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, Sq=16, Sk=1024, D=64,
+                scale=0.125, causal=0, dtype=fa.FA_F16, n_split=4, workspace=W, workspace_bytes=1 << 20,
+                stream=0)
+    args.update(kw)
+    return fa.fa_fwd_split(**args)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(lse=0), dict(o=A + 8), dict(Sk=0), dict(scale=float("nan")),
+    dict(n_split=-1), dict(workspace=0), dict(workspace=W + 8),
+    dict(workspace_bytes=4 * 16 * 65 * 4 - 1),           # one byte short
+    dict(workspace=A - 4096),                            # overlaps q
+    dict(workspace=4 * A), dict(workspace=5 * A - 1024),  # overlaps o, lse
+])
+def test_split_invalid_arguments(fa, kw):
+    assert _call_split(fa, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(D=96), dict(dtype=2)])
+def test_split_unsupported(fa, kw):
+    assert _call_split(fa, **kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def _call_merge(fa, **kw):
+    args = dict(o_parts=A, lse_parts=2 * A, n_part=3, rows=100, D=64, o=3 * A, lse=4 * A, dtype=fa.FA_BF16,
+                stream=0)
+    args.update(kw)
+    return fa.fa_lse_merge(**args)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(o_parts=0), dict(lse_parts=0), dict(o=0), dict(lse=0),
+    dict(o_parts=A + 4), dict(o=3 * A + 8), dict(lse=4 * A + 2),
+    dict(n_part=0), dict(rows=0), dict(D=0),
+    dict(o=A + 3 * 100 * 64 * 4 - 16),                 # overlaps the O parts
+    dict(lse=2 * A + 8),                               # overlaps the lse parts
+    dict(lse=3 * A + 100 * 64 * 2 - 4),                # overlaps o
+])
+def test_merge_invalid_arguments(fa, kw):
+    assert _call_merge(fa, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(D=32), dict(D=256), dict(dtype=5)])
+def test_merge_unsupported(fa, kw):
+    assert _call_merge(fa, **kw) == fa.FA_ERR_UNSUPPORTED
+

@@ -4,6 +4,8 @@ The compute path is the HIP library ``libfa_mi355x.so`` (C ABI in
 ``include/fa.h``); :mod:`tile_level_programming_amd.fa` is its ctypes binding.
 """
 
-from .fa import FA_BF16, FA_F16, FaError, fa_fwd, fa_status_string, fwd  # noqa: F401
+from .fa import (FA_BF16, FA_F16, FaError, fa_fwd, fa_fwd_split, fa_lse_merge, fa_status_string,  # noqa: F401
+                 fwd, fwd_split, lse_merge, split_count, split_workspace_size)
 
-__all__ = ["fa_fwd", "fa_status_string", "fwd", "FaError", "FA_F16", "FA_BF16"]
+__all__ = ["fa_fwd", "fa_fwd_split", "fa_lse_merge", "fa_status_string", "fwd", "fwd_split", "lse_merge",
+           "split_count", "split_workspace_size", "FaError", "FA_F16", "FA_BF16"]

@@ -105,6 +105,12 @@ struct Params {
   int n_wg;        // total work-groups
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 when scale < 0 (q is negated on load), else 0
+  // split over the keys: range r holds keys r*kchunk .. min(Sk, (r+1)*kchunk)-1
+  int n_split;     // ranges (1 without a split)
+  int kchunk;      // keys per range, a multiple of 64
+  int n_bh;        // B*H
+  float* po;       // partial O, fp32 [n_split][B*H*Sq][D], normalised over the range
+  float* plse;     // partial lse, fp32 [n_split][B*H*Sq]
 };
 
 template <bool BF16>
@@ -225,7 +231,7 @@ struct Flag { static constexpr bool value = B; };
 template <int I>
 struct Int { static constexpr int value = I; };
 
-template <int D, bool BF16, bool CAUSAL, int BN>
+template <int D, bool BF16, bool CAUSAL, int BN, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                     // bytes per row
@@ -265,29 +271,40 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   const int n = lane & 31;  // query column owned by this lane
   const int h = lane >> 5;  // which half of the wave
 
+  // logical block t = (bh * n_split + range) * n_qblk + query block: the
+  // query blocks that read the same keys are neighbours
   const int t = xcd_remap(blockIdx.x, p.n_wg);
-  const int bh = t / p.n_qblk;
-  int qblk = t - bh * p.n_qblk;
+  const int t2 = t / p.n_qblk;
+  int qblk = t - t2 * p.n_qblk;
+  const int split = SPLIT ? t2 % p.n_split : 0;
+  const int bh = SPLIT ? t2 / p.n_split : t2;
   if (CAUSAL) qblk = p.n_qblk - 1 - qblk;  // longest blocks first
   const int q0 = qblk * kBM;
   const int qw0 = q0 + wave * 32;  // first query of this wave
   const int qi = qw0 + n;          // query of this lane
 
-  const uint16_t* qg = p.q + (size_t)bh * p.Sq * D;
-  const uint16_t* kg = p.k + (size_t)bh * p.Sk * D;
-  const uint16_t* vg = p.v + (size_t)bh * p.Sk * D;
+  // the keys of this block: all of them, or (split) the Skl keys from kb0 on;
+  // tiles, masks and loads count keys from kb0
+  const int kb0 = SPLIT ? split * p.kchunk : 0;
+  const int Skl = SPLIT ? min(p.Sk - kb0, p.kchunk) : p.Sk;
+  const int qw0r = qw0 - kb0;  // query positions relative to kb0 (the causal
+  const int qir = qi - kb0;    // mask compares them with key positions)
 
-  const int kend = CAUSAL ? min(p.Sk, q0 + kBM) : p.Sk;
-  const int ntiles = (kend + BN - 1) / BN;
+  const uint16_t* qg = p.q + (size_t)bh * p.Sq * D;
+  const uint16_t* kg = p.k + ((size_t)bh * p.Sk + kb0) * D;
+  const uint16_t* vg = p.v + ((size_t)bh * p.Sk + kb0) * D;
+
+  const int kend = CAUSAL ? min(Skl, q0 - kb0 + kBM) : Skl;  // (split, causal: may be <= 0)
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
   // tiles this wave computes: all of the work-group's, less (causal) those
   // wholly above its last query; none for waves past the last query
-  int nt_w = CAUSAL ? min(ntiles, (qw0 + 31) / BN + 1) : ntiles;
+  int nt_w = CAUSAL ? (qw0r + 31 < 0 ? 0 : min(ntiles, (qw0r + 31) / BN + 1)) : ntiles;
   if (qw0 >= p.Sq) nt_w = 0;
   // the first tile that needs a mask: the one holding the end of the keys
-  // (when Sk is not a multiple of BN) or, causal, the first that reaches past
-  // this wave's first query
-  int j_mask = p.Sk / BN;
-  if (CAUSAL) j_mask = min(j_mask, (qw0 + 1) / BN);
+  // (when Skl is not a multiple of BN) or, causal, the first that reaches
+  // past this wave's first query
+  int j_mask = Skl / BN;
+  if (CAUSAL) j_mask = min(j_mask, qw0r + 1 <= 0 ? 0 : (qw0r + 1) / BN);
   // steps 0 .. j_fast-1 run branch-free: step j exponentiates tile j+1
   // (which must need no mask) and forms the scores of tile j+2 (which must
   // exist); a multiple of 4 steps, one per LDS stage
@@ -303,10 +320,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
     offv[i] = r * ROWB + ((pc ^ vsw<D>(r)) << 4);
   }
   auto issue_k = [&](int tile, char* buf) __attribute__((always_inline)) {
-    load_rows_to_lds<NLD>(kg, tile * BN, p.Sk, ROWB, buf + wave * 1024, kWaves * 1024, offk);
+    load_rows_to_lds<NLD>(kg, tile * BN, Skl, ROWB, buf + wave * 1024, kWaves * 1024, offk);
   };
   auto issue_v = [&](int tile, char* buf) __attribute__((always_inline)) {
-    load_rows_to_lds<NLD>(vg, tile * BN, p.Sk, ROWB, buf + wave * 1024, kWaves * 1024, offv);
+    load_rows_to_lds<NLD>(vg, tile * BN, Skl, ROWB, buf + wave * 1024, kWaves * 1024, offv);
   };
 
   // K 0 and K 1 first (the prologue's scores), then K 2 and V 0 (step 0),
@@ -391,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (key >= p.Sk || (CAUSAL && key > qi)) sacc[kb][r] = -INFINITY;
+        if (key >= Skl || (CAUSAL && key > qir)) sacc[kb][r] = -INFINITY;
       }
   };
 
@@ -597,12 +614,15 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NLD) : "memory");  // K 0, K 1 and K 2 have landed
   __syncthreads();
   if (nt_w > 0) {
-    // tile 0 from a zero reference; its row maximum becomes the reference
-    // (finite: key 0 is never masked)
+    // tile 0 from a zero reference; its row maximum becomes the reference.
+    // Key 0 of the range is masked only for a causal row that sees no key of
+    // the range at all (a split with i < kb0): that row keeps a zero
+    // reference, its P are all 0 and its sum stays 0.
     set_negm();
     score_tile(sa, kbuf(0));
     apply_mask(sa, 0);
     m_ref = tile_max(sa);
+    if (SPLIT && CAUSAL && m_ref == -INFINITY) m_ref = 0.f;
     set_negm();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -636,7 +656,27 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: normalise, round, store O rows and lse
-  if (qw0 < p.Sq) {
+  if (SPLIT && qi < p.Sq) {
+    // the range's partial result, fp32: O normalised over the range's keys
+    // and its lse; a row that sees none of them gets 0 and -inf (zero
+    // weight in the merge)
+    const float l = l_run;
+    const size_t row = ((size_t)split * p.n_bh + bh) * p.Sq + qi;
+    const float inv = l == 0.f ? 0.f : 1.f / l;
+    float* op = p.po + row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = db * 32 + 8 * gq + 4 * h;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * gq + e] * inv;
+        *reinterpret_cast<f32x4*>(op + d0) = w;
+      }
+    if (h == 0) p.plse[row] = l == 0.f ? -INFINITY : (m_ref * c + __log2f(l)) * kLn2;
+  }
+  if (!SPLIT && qw0 < p.Sq) {
     const float l = l_run;
     if (qi < p.Sq) {
       const float inv = 1.f / l;
@@ -662,15 +702,76 @@ struct Cfg {
   static constexpr int BN = D == 64 ? 64 : 32;
 };
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool SPLIT>
 hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream) {
   using C = Cfg<D, BF16, CAUSAL>;
   Params p = base;
   p.n_qblk = (int)((Sq + kBM - 1) / kBM);
-  p.n_wg = (int)(BH * p.n_qblk);
+  p.n_wg = (int)(BH * p.n_qblk * p.n_split);
   void* args[] = {&p};
-  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN>);
+  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN, SPLIT>);
   return hipLaunchKernel(fn, dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
+}
+
+template <bool SPLIT>
+hipError_t launch_any(const Params& p, int64_t BH, int64_t Sq, int64_t D, bool bf, bool causal, hipStream_t s) {
+  if (D == 64) {
+    if (bf) return causal ? launch<64, true, true, SPLIT>(p, BH, Sq, s) : launch<64, true, false, SPLIT>(p, BH, Sq, s);
+    return causal ? launch<64, false, true, SPLIT>(p, BH, Sq, s) : launch<64, false, false, SPLIT>(p, BH, Sq, s);
+  }
+  if (bf) return causal ? launch<128, true, true, SPLIT>(p, BH, Sq, s) : launch<128, true, false, SPLIT>(p, BH, Sq, s);
+  return causal ? launch<128, false, true, SPLIT>(p, BH, Sq, s) : launch<128, false, false, SPLIT>(p, BH, Sq, s);
+}
+
+// Log-sum-exp merge of partial results over disjoint key ranges (the online
+// softmax's rescaling to a common maximum, applied to finished partials):
+//   M = max_g lse_g,  lse = M + ln sum_g e^(lse_g - M),  o = sum_g e^(lse_g - lse) o_g
+// rounded to the storage type.  Parts with lse_g = -inf weigh nothing; a row
+// with only such parts gets lse = -inf and o = 0.  D/4 threads per row, 4
+// consecutive elements each (16-byte loads of every part).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float* po, const float* plse, int n_part,
+                                                       int64_t rows, uint16_t* o, float* lse) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int d0 = (threadIdx.x % TPR) * 4;
+  if (row >= rows) return;
+  float M = -INFINITY;
+  for (int g = 0; g < n_part; ++g) M = __builtin_elementwise_maximum(M, plse[(int64_t)g * rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = -INFINITY;
+  if (M != -INFINITY) {
+    float sum = 0.f;
+    for (int g = 0; g < n_part; ++g) sum += expf(plse[(int64_t)g * rows + row] - M);
+    L = M + logf(sum);
+    for (int g = 0; g < n_part; ++g) {
+      const float w = expf(plse[(int64_t)g * rows + row] - L);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(po + ((int64_t)g * rows + row) * D + d0);
+      acc += w * x;
+    }
+  }
+  u32x2 out;
+  out[0] = pack2<BF16>(acc[0], acc[1]);
+  out[1] = pack2<BF16>(acc[2], acc[3]);
+  *reinterpret_cast<u32x2*>(o + row * D + d0) = out;
+  if (d0 == 0) lse[row] = L;
+}
+
+hipError_t launch_merge(const float* po, const float* plse, int64_t n_part, int64_t rows, int64_t D, bool bf,
+                        void* o, float* lse, hipStream_t s) {
+  const int rpb = (int)(256 / (D / 4));
+  const int64_t blocks = (rows + rpb - 1) / rpb;
+  uint16_t* ob = static_cast<uint16_t*>(o);
+  const int np = (int)n_part;
+  if (D == 64) {
+    if (bf) lse_merge_kernel<64, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(po, plse, np, rows, ob, lse);
+    else lse_merge_kernel<64, false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(po, plse, np, rows, ob, lse);
+  } else {
+    if (bf) lse_merge_kernel<128, true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(po, plse, np, rows, ob, lse);
+    else lse_merge_kernel<128, false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(po, plse, np, rows, ob, lse);
+  }
+  return hipGetLastError();
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -678,11 +779,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-}  // namespace
-
-extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                            float scale, int causal, int dtype, void* stream) {
+// Host-side checks shared by the entry points: pointers, sizes, index
+// ranges and overlaps of the attention arguments (no device access).
+fa_status check_attention_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D, float scale,
+                               int dtype) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) || ((uintptr_t)lse & 3u))
     return FA_ERR_INVALID_ARG;
@@ -694,8 +795,7 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
   if (Sq >= lim / D || Sk >= lim / D) return FA_ERR_INVALID_ARG;
   if (B >= lim / H) return FA_ERR_INVALID_ARG;
   const int64_t BH = B * H;
-  const int64_t minBM = kBM;  // queries per work-group
-  if (BH >= lim / ((Sq + minBM - 1) / minBM)) return FA_ERR_INVALID_ARG;
+  if (BH >= lim / ((Sq + kBM - 1) / kBM)) return FA_ERR_INVALID_ARG;
   // element counts in int64: BH < 2^31 and S*D < 2^31 keep these below 2^62
   const size_t qo_bytes = (size_t)(BH * Sq * D) * 2, kv_bytes = (size_t)(BH * Sk * D) * 2;
   const size_t lse_bytes = (size_t)(BH * Sq) * 4;
@@ -704,7 +804,11 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
       overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes) ||
       overlaps(o, qo_bytes, lse, lse_bytes))
     return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
 
+Params make_params(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t Sq, int64_t Sk, float scale) {
   Params p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -717,17 +821,108 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
   p.n_wg = 0;
   p.c = (float)(fabs((double)scale) * 1.4426950408889634);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
+  p.n_split = 1;
+  p.kchunk = (int)Sk;
+  p.n_bh = (int)(B * H);
+  p.po = nullptr;
+  p.plse = nullptr;
+  return p;
+}
 
+// Key ranges of a split: the requested count (or, for 0, enough ranges to
+// give about kAutoSplitBlocks work-groups, with at least 256 keys each),
+// at least 64 keys per range; ranges are a multiple of 64 keys long, so the
+// count actually used may be smaller than the one asked for.
+constexpr int64_t kAutoSplitBlocks = 2048;
+struct SplitPlan {
+  int64_t n, chunk;
+};
+SplitPlan split_plan(int64_t BH, int64_t Sq, int64_t Sk, int64_t n_split) {
+  const int64_t wgs = BH * ((Sq + kBM - 1) / kBM);
+  int64_t n = n_split;
+  if (n <= 0) n = min((kAutoSplitBlocks + wgs - 1) / wgs, max((int64_t)1, Sk / 256));
+  n = max((int64_t)1, min(n, (Sk + 63) / 64));
+  const int64_t chunk = ((Sk + n - 1) / n + 63) / 64 * 64;
+  return {(Sk + chunk - 1) / chunk, chunk};
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                            float scale, int causal, int dtype, void* stream) {
+  const fa_status st = check_attention_args(q, k, v, o, lse, B, H, Sq, Sk, D, scale, dtype);
+  if (st != FA_OK) return st;
+  const Params p = make_params(q, k, v, o, lse, B, H, Sq, Sk, scale);
+  const hipError_t err =
+      launch_any<false>(p, B * H, Sq, D, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int64_t fa_fwd_split_count(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t n_split) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || n_split < 0) return 0;
+  return split_plan(B * H, Sq, Sk, n_split).n;
+}
+
+extern "C" size_t fa_fwd_split_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                              int64_t n_split) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1 || n_split < 0) return 0;
+  const int64_t n = split_plan(B * H, Sq, Sk, n_split).n;
+  return (size_t)n * (size_t)(B * H * Sq) * (size_t)(D + 1) * 4u;
+}
+
+extern "C" fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                  float scale, int causal, int dtype, int64_t n_split,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status st = check_attention_args(q, k, v, o, lse, B, H, Sq, Sk, D, scale, dtype);
+  if (st != FA_OK) return st;
+  if (n_split < 0 || !workspace || ((uintptr_t)workspace & 15u)) return FA_ERR_INVALID_ARG;
+  const int64_t BH = B * H;
+  const SplitPlan sp = split_plan(BH, Sq, Sk, n_split);
+  const int64_t lim = (int64_t)1 << 31;
+  if (BH * ((Sq + kBM - 1) / kBM) >= lim / sp.n) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_fwd_split_workspace_size(B, H, Sq, Sk, D, n_split);
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t qo_bytes = (size_t)(BH * Sq * D) * 2, kv_bytes = (size_t)(BH * Sk * D) * 2;
+  const size_t lse_bytes = (size_t)(BH * Sq) * 4;
+  if (overlaps(workspace, need, q, qo_bytes) || overlaps(workspace, need, k, kv_bytes) ||
+      overlaps(workspace, need, v, kv_bytes) || overlaps(workspace, need, o, qo_bytes) ||
+      overlaps(workspace, need, lse, lse_bytes))
+    return FA_ERR_INVALID_ARG;
+
+  Params p = make_params(q, k, v, o, lse, B, H, Sq, Sk, scale);
+  p.n_split = (int)sp.n;
+  p.kchunk = (int)sp.chunk;
+  p.po = static_cast<float*>(workspace);
+  p.plse = p.po + (size_t)sp.n * (size_t)(BH * Sq) * (size_t)D;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = dtype == FA_BF16;
-  hipError_t err;
-  if (D == 64) {
-    if (bf) err = causal ? launch<64, true, true>(p, BH, Sq, s) : launch<64, true, false>(p, BH, Sq, s);
-    else err = causal ? launch<64, false, true>(p, BH, Sq, s) : launch<64, false, false>(p, BH, Sq, s);
-  } else {
-    if (bf) err = causal ? launch<128, true, true>(p, BH, Sq, s) : launch<128, true, false>(p, BH, Sq, s);
-    else err = causal ? launch<128, false, true>(p, BH, Sq, s) : launch<128, false, false>(p, BH, Sq, s);
-  }
+  if (launch_any<true>(p, BH, Sq, D, bf, causal != 0, s) != hipSuccess) return FA_ERR_LAUNCH;
+  if (launch_merge(p.po, p.plse, sp.n, BH * Sq, D, bf, o, lse, s) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+extern "C" fa_status fa_lse_merge(const float* o_parts, const float* lse_parts, int64_t n_part, int64_t rows,
+                                  int64_t D, void* o, float* lse, int dtype, void* stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_INVALID_ARG;
+  if ((((uintptr_t)o_parts | (uintptr_t)o) & 15u) || (((uintptr_t)lse_parts | (uintptr_t)lse) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (n_part < 1 || rows < 1 || D < 1) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if (n_part >= lim || rows >= ((int64_t)1 << 40) / D || n_part >= ((int64_t)1 << 52) / (rows * D))
+    return FA_ERR_INVALID_ARG;
+  if ((rows + 255) / (256 / (D / 4)) >= lim) return FA_ERR_INVALID_ARG;
+  const size_t po_bytes = (size_t)(n_part * rows * D) * 4, pl_bytes = (size_t)(n_part * rows) * 4;
+  const size_t o_bytes = (size_t)(rows * D) * 2, l_bytes = (size_t)rows * 4;
+  if (overlaps(o, o_bytes, o_parts, po_bytes) || overlaps(o, o_bytes, lse_parts, pl_bytes) ||
+      overlaps(lse, l_bytes, o_parts, po_bytes) || overlaps(lse, l_bytes, lse_parts, pl_bytes) ||
+      overlaps(o, o_bytes, lse, l_bytes))
+    return FA_ERR_INVALID_ARG;
+  const hipError_t err =
+      launch_merge(o_parts, lse_parts, n_part, rows, D, dtype == FA_BF16, o, lse, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

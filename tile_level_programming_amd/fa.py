@@ -24,7 +24,7 @@ FA_ERR_LAUNCH = 3
 
 class FaError(RuntimeError):
     def __init__(self, status: int):
-        super().__init__(f"fa_fwd failed: {fa_status_string(status)} (status {status})")
+        super().__init__(f"attention call failed: {fa_status_string(status)} (status {status})")
         self.status = status
 
 
@@ -40,6 +40,20 @@ def _load():
                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                            ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                            ctypes.c_void_p]
+    lib.fa_fwd_split_count.restype = ctypes.c_int64
+    lib.fa_fwd_split_count.argtypes = [ctypes.c_int64] * 5
+    lib.fa_fwd_split_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_split_workspace_size.argtypes = [ctypes.c_int64] * 6
+    lib.fa_fwd_split.restype = ctypes.c_int
+    lib.fa_fwd_split.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.fa_lse_merge.restype = ctypes.c_int
+    lib.fa_lse_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -58,8 +72,107 @@ def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int, Sk
     return int(_lib.fa_fwd(q, k, v, o, lse, B, H, Sq, Sk, D, scale, int(causal), int(dtype), stream))
 
 
+def fa_fwd_split(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int, Sk: int, D: int,
+                 scale: float, causal: int, dtype: int, n_split: int, workspace: int, workspace_bytes: int,
+                 stream: int) -> int:
+    """Direct call of the C entry point with raw device addresses; returns the status."""
+    return int(_lib.fa_fwd_split(q, k, v, o, lse, B, H, Sq, Sk, D, scale, int(causal), int(dtype),
+                                 int(n_split), workspace, int(workspace_bytes), stream))
+
+
+def fa_lse_merge(o_parts: int, lse_parts: int, n_part: int, rows: int, D: int, o: int, lse: int, dtype: int,
+                 stream: int) -> int:
+    """Direct call of the C entry point with raw device addresses; returns the status."""
+    return int(_lib.fa_lse_merge(o_parts, lse_parts, n_part, rows, D, o, lse, int(dtype), stream))
+
+
+def split_count(B: int, H: int, Sq: int, Sk: int, n_split: int = 0) -> int:
+    return int(_lib.fa_fwd_split_count(B, H, Sq, Sk, n_split))
+
+
+def split_workspace_size(B: int, H: int, Sq: int, Sk: int, D: int, n_split: int = 0) -> int:
+    return int(_lib.fa_fwd_split_workspace_size(B, H, Sq, Sk, D, n_split))
+
+
 def fa_status_string(status: int) -> str:
     return _lib.fa_status_string(int(status)).decode()
+
+
+def _check(q, k, v):
+    import torch
+
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("q, k, v must be float16 or bfloat16")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if tuple(k.shape) != (B, H, Sk, D) or tuple(v.shape) != (B, H, Sk, D):
+        raise ValueError("k and v must be [B, H, Sk, D] matching q")
+    return B, H, Sq, Sk, D
+
+
+def fwd_split(q, k, v, causal: bool = False, scale: float | None = None, n_split: int = 0, out=None,
+              lse=None, workspace=None):
+    """Attention forward split over the keys (fa_fwd_split), for small Sq and
+    long Sk.  ``workspace`` is a uint8 device tensor of at least
+    :func:`split_workspace_size` bytes (allocated with torch when None).
+    Returns (o, lse).  Runs on torch's current stream, no synchronisation.
+    """
+    import math
+
+    import torch
+
+    B, H, Sq, Sk, D = _check(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    need = split_workspace_size(B, H, Sq, Sk, D, n_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dt = FA_F16 if q.dtype == torch.float16 else FA_BF16
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, H, Sq, Sk, D, float(scale), int(causal), dt, int(n_split),
+                      workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return out, lse
+
+
+def lse_merge(o_parts, lse_parts, dtype):
+    """Merge fp32 partials o_parts [G, ..., D] and lse_parts [G, ...] into
+    (o [..., D] of torch dtype ``dtype``, lse float32 [...]) with fa_lse_merge."""
+    import torch
+
+    G, D = o_parts.shape[0], o_parts.shape[-1]
+    lead = tuple(lse_parts.shape[1:])
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if tuple(o_parts.shape) != (G, *lead, D) or lse_parts.shape[0] != G:
+        raise ValueError("o_parts must be [G, ..., D] and lse_parts [G, ...]")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    rows = 1
+    for x in lead:
+        rows *= int(x)
+    o = torch.empty((*lead, D), dtype=dtype, device=o_parts.device)
+    lse = torch.empty(lead, dtype=torch.float32, device=o_parts.device)
+    dt = FA_F16 if dtype == torch.float16 else FA_BF16
+    stream = torch.cuda.current_stream(o_parts.device).cuda_stream
+    st = fa_lse_merge(o_parts.data_ptr(), lse_parts.data_ptr(), G, rows, D, o.data_ptr(), lse.data_ptr(),
+                      dt, stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
