@@ -115,6 +115,7 @@ class Workload:
     seed: int
     sigma_qk: float = 1.0
     sigma_v: float = 1.0
+    split: bool = False  # run through the key-split entry point (decode-shaped calls)
 
     @property
     def scale(self) -> float:
@@ -159,6 +160,18 @@ WORKLOADS = {
                                                      "bf16", True, 5, sigma_qk=2.0, sigma_v=1.0),
 }
 HEADLINE = "b2h32_s8192_d64_f16"
+
+# Decode-shaped calls (a few queries per head against a long key sequence),
+# run through the key-split entry point: one work-group per (batch, head,
+# query block) would occupy a small part of the GPU, and the time is the one
+# pass over K and V, so these are HBM-bound.  Non-causal, i.i.d. normal.
+DECODE_WORKLOADS = {
+    "decode_b16h32_sq1_sk16384_d128_bf16": Workload("decode_b16h32_sq1_sk16384_d128_bf16", 16, 32, 1, 16384, 128,
+                                                    "bf16", False, 6, split=True),
+    "decode_b8h32_sq16_sk32768_d64_f16": Workload("decode_b8h32_sq16_sk32768_d64_f16", 8, 32, 16, 32768, 64,
+                                                  "f16", False, 7, split=True),
+}
+ALL_WORKLOADS = {**WORKLOADS, **DECODE_WORKLOADS}
 
 
 def make_inputs(w: Workload):

@@ -162,3 +162,27 @@ def test_split_deterministic_and_matches_unsplit(torch_dev, fa, oracle_mod):
     torch.cuda.synchronize()
     assert (o1.float() - o3.float()).abs().max().item() <= TOL_O[dtype]
     assert ((l1 - l3).abs() / l3.abs().clamp(min=1.0)).max().item() <= TOL_LSE
+
+
+@pytest.mark.parametrize("name", list(fi.DECODE_WORKLOADS))
+def test_decode_workload_parity(torch_dev, fa, oracle_mod, name):
+    # the benchmarked decode shapes, at full size and in the launch
+    # configuration the benchmark times (automatic range count), on sampled
+    # rows the oracle evaluates one by one
+    torch = torch_dev
+    w = fi.DECODE_WORKLOADS[name]
+    print(f"[split] workload {name}", flush=True)
+    q, k, v = fi.make_inputs(w)
+    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    qd, kd, vd = (torch.from_numpy(x.view(np.int16)).view(tdt).cuda() for x in (q, k, v))
+    o, lse = fa.fwd_split(qd, kd, vd, causal=w.causal, scale=w.scale, n_split=0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    n_rows = w.B * w.H * w.Sq
+    rows = np.unique(np.concatenate([[0, 1, n_rows - 1], rng.integers(0, n_rows, 96)]))
+    idx = torch.from_numpy(rows).cuda()
+    o_s = o.view(-1, w.D)[idx].double().cpu().numpy()
+    l_s = lse.view(-1)[idx].double().cpu().numpy()
+    o_ref, l_ref = oracle_mod.attention_rows(q, k, v, w.dtype, w.scale, w.causal, rows, threads=THREADS)
+    check(o_s, l_s, o_ref, l_ref, w.dtype, name)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
