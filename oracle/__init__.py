@@ -32,11 +32,15 @@ DTYPE_CODE = {"f16": 0, "bf16": 1}
 
 
 def build() -> str:
-    """Compile the oracle with gcc (plain -O2, no fast-math, no FP contraction)."""
+    """Compile the oracles with gcc (plain -O2, no fast-math, no FP contraction):
+    the attention oracle here and the GEMM + bias + GELU oracle of ``oracle.gemm``."""
     cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
            "-std=c11", "-Wall", "-Wextra", _SRC, "-o", _LIB + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
+    from . import gemm
+
+    gemm.build()
     return _LIB
 
 
