@@ -174,6 +174,47 @@ DECODE_WORKLOADS = {
 ALL_WORKLOADS = {**WORKLOADS, **DECODE_WORKLOADS}
 
 
+@dataclasses.dataclass(frozen=True)
+class GemmWorkload:
+    """C = gelu(A W^T + bias): A [M, K], W [N, K], bias [N], i.i.d. N(0, sigma^2)."""
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str
+    seed: int
+    sigma: float = 1.0
+    bias: bool = True
+
+    def flops(self) -> int:
+        """Algorithmic FLOP of the product (the epilogue is not counted): 2*M*N*K."""
+        return 2 * self.M * self.N * self.K
+
+    def io_bytes(self) -> int:
+        """A, W and bias read once, C written once."""
+        return 2 * (self.M * self.K + self.N * self.K + (self.N if self.bias else 0) + self.M * self.N)
+
+
+def make_gemm_inputs(w: GemmWorkload):
+    """(a, w, bias or None) uint16 bit-pattern arrays for a GEMM workload.  The
+    inputs are scaled by 1/sqrt(K) on the weight side, so that the
+    pre-activations are O(1) as in a trained layer and the GELU is not
+    saturated."""
+    a = tensor_bits(w.seed, "a", (w.M, w.K), w.dtype, w.sigma)
+    wt = tensor_bits(w.seed, "w", (w.N, w.K), w.dtype, w.sigma / math.sqrt(w.K))
+    b = tensor_bits(w.seed, "bias", (w.N,), w.dtype, w.sigma) if w.bias else None
+    return a, wt, b
+
+
+# GEMM with the fused bias + GELU epilogue.  The pages name no shapes (their
+# example tile is 128 x 128 x 32); these are the up-projection of a
+# transformer MLP (8192 tokens, 4096 -> 16384) and a square one.
+GEMM_WORKLOADS = {
+    "gemm_m8192_n16384_k4096_bf16": GemmWorkload("gemm_m8192_n16384_k4096_bf16", 8192, 16384, 4096, "bf16", 8),
+    "gemm_m4096_n4096_k4096_f16": GemmWorkload("gemm_m4096_n4096_k4096_f16", 4096, 4096, 4096, "f16", 9),
+}
+
+
 def make_inputs(w: Workload):
     """(q, k, v) uint16 bit-pattern arrays for a workload."""
     q = tensor_bits(w.seed, "q", w.shape_q(), w.dtype, w.sigma_qk)

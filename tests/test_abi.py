@@ -30,7 +30,7 @@ def fa():
 
 def test_header_declares_entry_points():
     assert _declared_functions() == ["fa_fwd", "fa_fwd_split", "fa_fwd_split_count", "fa_fwd_split_workspace_size",
-                                     "fa_lse_merge", "fa_status_string"]
+                                     "fa_lse_merge", "fa_status_string", "gemm_bias_gelu"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -161,4 +161,27 @@ def test_merge_invalid_arguments(fa, kw):
 @pytest.mark.parametrize("kw", [dict(D=32), dict(D=256), dict(dtype=5)])
 def test_merge_unsupported(fa, kw):
     assert _call_merge(fa, **kw) == fa.FA_ERR_UNSUPPORTED
+
+
+# --- GEMM with the fused bias + GELU epilogue: host-side checks --------------
+
+
+def _call_gemm(fa, **kw):
+    args = dict(a=A, w=2 * A, bias=3 * A, c=4 * A, M=100, N=64, K=64, dtype=fa.FA_F16, stream=0)
+    args.update(kw)
+    return fa.gemm_bias_gelu(**args)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(a=0), dict(w=0), dict(c=0), dict(a=A + 8), dict(w=2 * A + 4), dict(c=4 * A + 2), dict(bias=3 * A + 1),
+    dict(M=0), dict(N=0), dict(K=0), dict(M=-5), dict(M=1 << 31), dict(K=1 << 24),
+    dict(c=A + 96), dict(c=2 * A - 64), dict(c=3 * A - 16),   # overlaps a, w, bias
+])
+def test_gemm_invalid_arguments(fa, kw):
+    assert _call_gemm(fa, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(K=12), dict(K=100), dict(dtype=3)])
+def test_gemm_unsupported(fa, kw):
+    assert _call_gemm(fa, **kw) == fa.FA_ERR_UNSUPPORTED
 

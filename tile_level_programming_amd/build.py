@@ -1,7 +1,8 @@
 """Compile the HIP library for gfx950, in-tree.
 
-The library is one HIP translation unit plus the C ABI declared in
-``include/fa.h``; it is built with hipcc for gfx950 only, with packed fp32
+The library is two HIP translation units (attention; GEMM with a fused bias +
+GELU epilogue) with the C ABI declared in ``include/fa.h`` and
+``include/gemm.h``; it is built with hipcc for gfx950 only, with packed fp32
 instructions disabled in device code.
 """
 
@@ -14,6 +15,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
+SRCS = [SRC, os.path.join(PKG, "csrc", "gemm_bias_gelu.hip")]
 LIB = os.path.join(PKG, "libfa_mi355x.so")
 ARCH = "gfx950"
 
@@ -32,7 +34,7 @@ def hipcc() -> str:
 
 
 def build(extra=None, out=LIB) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), SRC, "-o", out + ".tmp"]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), *SRCS, "-o", out + ".tmp"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out

@@ -1,8 +1,10 @@
-"""ctypes binding of the C ABI in include/fa.h (argument marshalling only).
+"""ctypes binding of the C ABI in include/fa.h and include/gemm.h (argument
+marshalling only).
 
-Every step of the attention forward pass runs in the HIP library
-``libfa_mi355x.so``; this module only loads it, converts arguments and, in
-:func:`fwd`, allocates the outputs with torch.  There is no fallback: if the
+Every step of the attention forward pass and of the GEMM with its fused
+bias + GELU epilogue runs in the HIP library ``libfa_mi355x.so``; this module
+only loads it, converts arguments and, in the torch-level helpers, allocates
+outputs (and the split workspace) with torch.  There is no fallback: if the
 library is missing, importing the binding raises.
 """
 
@@ -54,6 +56,9 @@ def _load():
     lib.fa_lse_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                  ctypes.c_void_p]
+    lib.gemm_bias_gelu.restype = ctypes.c_int
+    lib.gemm_bias_gelu.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -84,6 +89,40 @@ def fa_lse_merge(o_parts: int, lse_parts: int, n_part: int, rows: int, D: int, o
                  stream: int) -> int:
     """Direct call of the C entry point with raw device addresses; returns the status."""
     return int(_lib.fa_lse_merge(o_parts, lse_parts, n_part, rows, D, o, lse, int(dtype), stream))
+
+
+def gemm_bias_gelu(a: int, w: int, bias: int, c: int, M: int, N: int, K: int, dtype: int, stream: int) -> int:
+    """Direct call of the C entry point with raw device addresses (bias 0 = none); returns the status."""
+    return int(_lib.gemm_bias_gelu(a, w, bias or None, c, M, N, K, int(dtype), stream))
+
+
+def linear_gelu(a, w, bias=None, out=None):
+    """gelu(a @ w.T + bias) on torch device tensors: a [M, K], w [N, K], bias [N]
+    (or None), fp16 or bf16; returns c [M, N].  Runs on torch's current stream."""
+    import torch
+
+    if a.dtype not in (torch.float16, torch.bfloat16) or w.dtype != a.dtype:
+        raise TypeError("a and w must share one dtype, float16 or bfloat16")
+    if bias is not None and bias.dtype != a.dtype:
+        raise TypeError("bias must have the dtype of a")
+    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1]:
+        raise ValueError("a must be [M, K] and w [N, K]")
+    M, K = a.shape
+    N = w.shape[0]
+    if bias is not None and tuple(bias.shape) != (N,):
+        raise ValueError("bias must be [N]")
+    for t in (a, w) + ((bias,) if bias is not None else ()):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("a, w, bias must be contiguous device tensors")
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    dt = FA_F16 if a.dtype == torch.float16 else FA_BF16
+    stream = torch.cuda.current_stream(a.device).cuda_stream
+    st = gemm_bias_gelu(a.data_ptr(), w.data_ptr(), 0 if bias is None else bias.data_ptr(), out.data_ptr(),
+                        M, N, K, dt, stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return out
 
 
 def split_count(B: int, H: int, Sq: int, Sk: int, n_split: int = 0) -> int:
