@@ -7,7 +7,8 @@ softmax, P.V, normalisation, lse) over the workload's seeded inputs, which are
 resident in device memory before timing starts.  Prints one JSON line.  The
 decode-shaped workloads (few queries, long keys) run one fa_fwd_split call per
 step instead: the partial-result kernel over the key ranges and the merge,
-with the workspace allocated before timing.
+with the workspace allocated before timing.  The gemm_* workloads time one
+gemm_bias_gelu call per step (C = gelu(A W^T + bias)).
 
 Reported alongside the throughput:
   * roofline: the attention kernel against the dense fp16/bf16 MFMA peak,
@@ -42,6 +43,7 @@ PEAK_TFLOPS_F16 = 2516.6
 # MI355X HBM3E peak bandwidth (8 TB/s).
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "tile_level_programming_amd", "csrc", "fa_fwd.hip")
+GEMM_SRC = os.path.join(ROOT, "tile_level_programming_amd", "csrc", "gemm_bias_gelu.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -49,18 +51,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
-    """sha256[:16] of the kernel source with // comments and blank lines removed:
-    counters taken on a source stay valid across comment edits, not code edits."""
+def kernel_hash(path: str | None = None) -> str:
+    """sha256[:16] of a kernel source (the attention one by default) with //
+    comments and blank lines removed: counters taken on a source stay valid
+    across comment edits, not code edits."""
     import re
 
-    with open(KERNEL_SRC, encoding="utf-8") as f:
+    with open(path or KERNEL_SRC, encoding="utf-8") as f:
         lines = [re.sub(r"\s*//.*$", "", ln).rstrip() for ln in f]
     code = "\n".join(ln for ln in lines if ln)
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def traffic_for(workload: str):
+def traffic_for(workload: str, src: str | None = None):
     """HBM bytes per launch measured by rocprofv3 on this kernel source, or None."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -68,7 +71,7 @@ def traffic_for(workload: str):
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("kernel_sha256_16") != kernel_hash():
+    if not ent or ent.get("kernel_sha256_16") != kernel_hash(src):
         return None
     return ent.get("bytes_per_launch")
 
@@ -105,12 +108,130 @@ def cpu_baseline(w, q, k, v, seconds: float, threads: int):
     }
 
 
+def gemm_cpu_baseline(w, a, wt, b, seconds: float, threads: int):
+    import oracle.gemm as og
+
+    per_row_flop = 2 * w.N * w.K
+    rng = np.random.default_rng(4321)
+    n = threads
+    while True:
+        rows = rng.integers(0, w.M, n)
+        t0 = time.perf_counter()
+        og.gemm_rows(a, wt, b, w.dtype, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= 1.0 or n >= w.M:
+            break
+        n *= 4
+    n = int(max(threads, min(w.M, n * seconds / max(dt, 1e-6))))
+    rows = rng.integers(0, w.M, n)
+    t0 = time.perf_counter()
+    og.gemm_rows(a, wt, b, w.dtype, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(n * per_row_flop / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n} seeded random output rows of {w.name} ({n / w.M:.2%} of the rows, all {w.N} columns each), "
+                  f"float64, {dt:.1f} s wall",
+    }
+
+
+def run_gemm(args, w):
+    """One step = one gemm_bias_gelu call: C = gelu(A W^T + bias)."""
+    import torch
+
+    from tile_level_programming_amd import fa
+
+    log(f"[bench] workload {w.name}: generating seeded inputs")
+    a, wt, b = fi.make_gemm_inputs(w)
+    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    ad, wd = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (a, wt))
+    bd = torch.from_numpy(b.view(np.int16)).view(tdt).to(dev) if b is not None else None
+    c = torch.empty((w.M, w.N), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    dt_code = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
+
+    def step():
+        st = fa.gemm_bias_gelu(ad.data_ptr(), wd.data_ptr(), 0 if bd is None else bd.data_ptr(), c.data_ptr(),
+                               w.M, w.N, w.K, dt_code, sp)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start.record(stream)
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms_kernel = float(np.mean(launch_ms))
+    flop = w.flops()
+    tflops = flop / (ms * 1e-3) / 1e12
+    tflops_kernel = flop / (ms_kernel * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s; per launch mean {ms_kernel:.4f} ms "
+        f"(min {min(launch_ms):.4f}, max {max(launch_ms):.4f}), {tflops_kernel:.1f} TFLOP/s")
+
+    import oracle.gemm as og
+
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, w.M - 1], rng.integers(0, w.M, 30)]))
+    cs = c[torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+    threads = min(16, os.cpu_count() or 1)
+    ref = og.gemm_rows(a, wt, b, w.dtype, rows=rows, threads=threads)
+    rel = 2.0 ** -10 if w.dtype == "f16" else 2.0 ** -7
+    err = float((np.abs(cs - ref) / np.maximum(np.abs(ref), 1.0)).max())
+    parity_ok = bool(err <= rel and np.isfinite(cs).all())
+    log(f"[bench] sampled parity: max |dC|/max(|C|,1) = {err:.2e} (bar {rel:.2e}) ok={parity_ok}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {threads} threads, ~{args.cpu_seconds:.0f} s")
+        cpu = gemm_cpu_baseline(w, a, wt, b, args.cpu_seconds, threads)
+    line = {
+        "metric": "GEMM + bias + GELU TFLOP/s and % of MI355X dense fp16/bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded i.i.d. normal A; W normal with sigma 1/sqrt(K); normal bias)",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "bias": w.bias, "algorithmic_flop": flop,
+                   "algorithmic_bytes": w.io_bytes(), "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS_F16, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": PEAK_TFLOPS_F16,
+                     "unit": "TFLOP/s", "frac": round(tflops_kernel / PEAK_TFLOPS_F16, 4),
+                     "traffic": traffic_for(w.name, GEMM_SRC), "kernel_ms": round(ms_kernel, 5),
+                     "algorithmic_flop_per_launch": flop},
+        "cpu_baseline": cpu,
+        "parity_sample": {"rows": int(rows.size), "max_rel_err": err, "bar": rel, "ok": parity_ok},
+        "kernel_sha256_16": kernel_hash(GEMM_SRC),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=fi.HEADLINE, choices=list(fi.ALL_WORKLOADS))
+    ap.add_argument("--workload", default=fi.HEADLINE, choices=list(fi.ALL_WORKLOADS) + list(fi.GEMM_WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -138,6 +259,9 @@ def main():
         log(f"[bench] copy probe: 10 copies of {n} bytes (read {n} B + write {n} B each)")
         return
 
+    if args.workload in fi.GEMM_WORKLOADS:
+        run_gemm(args, fi.GEMM_WORKLOADS[args.workload])
+        return
     w = fi.ALL_WORKLOADS[args.workload]
     log(f"[bench] workload {w.name}: generating seeded inputs")
     q, k, v = fi.make_inputs(w)

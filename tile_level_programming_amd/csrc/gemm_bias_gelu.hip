@@ -13,28 +13,33 @@
 // A [M, K], W [N, K] (the weight layout of a linear layer), bias [N] and C
 // [M, N], row-major, fp16 or bf16, accumulation in fp32.
 //
-// CDNA4 mapping.  One work-group of four waves owns a 128 x 128 tile of C;
-// each wave a 64 x 64 quarter, as 2 x 2 blocks of v_mfma_f32_32x32x16.  The
-// products are formed transposed, C^T = W A^T: the W fragment is the A
-// operand and the A fragment the B operand, so a lane owns one row m of C
-// and holds 16 of its columns n in runs of 4 consecutive ones (8-byte
-// stores in the epilogue).  Both fragments are 16-byte reads of K-contiguous
-// rows.
+// CDNA4 mapping.  One work-group of eight waves (two per SIMD) owns a
+// 256 x 256 tile of C; the waves form a 4 (n) x 2 (m) grid, each owning 64
+// columns n by 128 rows m as 2 x 4 blocks of v_mfma_f32_32x32x16 (128
+// accumulator registers).  The products are formed transposed, C^T = W A^T:
+// the W fragment is the A operand and the A fragment the B operand, so a
+// lane owns one row m of C and holds 16 of its columns n per block in runs
+// of 4 consecutive ones (8-byte stores in the epilogue).  Both fragments are
+// 16-byte reads of K-contiguous rows.
 //
-//  * K is streamed in 32-wide slabs through a ring of four LDS stages
-//    (A and W slab of a stage: 8 KiB each), loaded three slabs ahead with
-//    buffer_load_dwordx4 straight into LDS.  Each lane picks the global
-//    16-byte chunk that belongs at its LDS slot, which lays a row's four
-//    chunks out XOR-swizzled (chunk c of row r at c ^ ((r >> 2) & 3)): the
-//    fragment reads of 16 consecutive rows then hit all 64 banks once.
+//  * K is streamed in 32-wide slabs through a ring of four LDS stages (A and
+//    W slab of a stage: 16 KiB each, 128 KiB in all), loaded three slabs
+//    ahead with buffer_load_dwordx4 straight into LDS.  Each lane picks the
+//    global 16-byte chunk that belongs at its LDS slot, which lays a row's
+//    four chunks out XOR-swizzled (chunk c of row r at c ^ ((r >> 2) & 3)):
+//    the fragment reads of 16 consecutive rows then hit all 64 banks once.
+//    The first k-step's fragments of the next slab are read at the end of
+//    each step, so a step's products start without waiting for LDS.
 //  * Rows past M or N lie outside the buffer range and read as zeros;
 //    chunks past K get an offset outside the range and read as zeros.
 //    Slabs past the end are loaded as zeros too, so every wait has a fixed
 //    count.
 //  * Work-group ids are remapped so that each XCD runs a contiguous range of
-//    tiles, ordered in groups of 8 tile rows: the tiles running together
-//    share rows of A and W in their XCD's L2.
-//  * Epilogue: acc + bias[n], gelu in fp32 (erff), rounded to nearest even.
+//    tiles, ordered in groups of 4 tile rows (column-major inside a group):
+//    the 32 tiles an XCD runs together are 4 rows by 8 columns of tiles, and
+//    share rows of A and W in its L2.
+//  * Epilogue: acc + bias[n] (read before the K loop), gelu in fp32 with the
+//    Abramowitz-Stegun erf approximation, rounded to nearest even.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -55,10 +60,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // a buffer offset past any range: reads zeros
-constexpr int kWaves = 4;
-constexpr int kBM = 128, kBN = 128, kBK = 32;   // work-group tile and K slab
-constexpr int kStages = 4;
-constexpr int kGroupM = 8;                      // tile rows per ordering group
+constexpr int kGroupM = 4;                      // tile rows per ordering group
+
+// Tile configuration: a work-group of WGN x WGM waves (n x m), each wave
+// owning WTN x WTM blocks of 32 x 32; K is streamed in BK-wide slabs through
+// NST LDS stages, loaded NST-1 slabs ahead.
+struct Cfg {
+  static constexpr int WGN = 4, WGM = 2, WTN = 2, WTM = 4, BK = 32, NST = 4;
+  static constexpr int BN = 32 * WTN * WGN, BM = 32 * WTM * WGM, NW = WGN * WGM;
+};
 
 struct GemmParams {
   const uint16_t* a;
@@ -105,8 +115,35 @@ __device__ __forceinline__ uint16_t round1(float a) {
   return (uint16_t)(pack2<BF16>(a, 0.f) & 0xFFFFu);
 }
 
+// gelu(x) = x * Phi(x).  Phi from the erf approximation 7.1.26 of
+// Abramowitz and Stegun (|error of erf| <= 1.5e-7 for all x), applied to
+// |x|/sqrt(2):  h = 1 - Phi(|x|) = (a1 t + a2 t^2 + ... + a5 t^5) e^(-x^2/2) / 2
+// with t = 1 / (1 + p |x|/sqrt(2)); Phi(x) = 1 - h for x >= 0 and h for
+// x < 0 (no cancellation in the negative tail).  About a dozen instructions
+// and no branch; the error (<= 7.5e-8 |x|) is far below the output rounding.
 __device__ __forceinline__ float gelu(float x) {
-  return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.f));
+  float poly = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  poly = __builtin_fmaf(poly, t, 1.421413741f);
+  poly = __builtin_fmaf(poly, t, -0.284496736f);
+  poly = __builtin_fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);  // e^(-z^2)
+  const float h = 0.5f * poly * e;
+  return x * (x >= 0.f ? 1.f - h : h);
+}
+
+template <int I>
+struct Int { static constexpr int value = I; };
+
+// f(Int<I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Int<B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 __device__ __forceinline__ int xcd_remap(int wg, int n) {
@@ -116,23 +153,35 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   return base + local;
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(256, 2) void gemm_bias_gelu_kernel(GemmParams p) {
-  constexpr int SLAB = kBM * kBK * 2;               // bytes of one A (or W) slab
-  constexpr int NLD = SLAB / 16 / (64 * kWaves);    // loads per wave per slab and matrix (2)
-  __shared__ u32x4 as0[SLAB / 16], as1[SLAB / 16], as2[SLAB / 16], as3[SLAB / 16];
-  __shared__ u32x4 ws0[SLAB / 16], ws1[SLAB / 16], ws2[SLAB / 16], ws3[SLAB / 16];
+template <bool BF16, int WGN, int WGM, int WTN, int WTM, int BK, int NST>
+__global__ __launch_bounds__(64 * WGN * WGM) void gemm_bias_gelu_kernel(GemmParams p) {
+  constexpr int kWaves = WGN * WGM;
+  constexpr int BN = 32 * WTN * WGN, BM = 32 * WTM * WGM;
+  constexpr int ROWB = BK * 2;                 // bytes of a slab row
+  constexpr int CPR = BK / 8;                  // 16-byte chunks per slab row
+  constexpr int RPL = 256 / ROWB;              // slab rows per 256-byte bank line
+  constexpr int ASLAB = BM * ROWB, WSLAB = BN * ROWB;
+  constexpr int NLA = ASLAB / (16 * 64 * kWaves), NLW = WSLAB / (16 * 64 * kWaves);  // loads per wave
+  static_assert(NST >= 3 && NST <= 4, "three or four stages");
+  static_assert(NLA * 16 * 64 * kWaves == ASLAB && NLW * 16 * 64 * kWaves == WSLAB, "slabs split over the waves");
+  // one array per stage and matrix: the compiler can then tell that the
+  // loads streaming into one stage never alias the reads from another
+  __shared__ u32x4 as0[ASLAB / 16], as1[ASLAB / 16], as2[NST > 2 ? ASLAB / 16 : 1], as3[NST > 3 ? ASLAB / 16 : 1];
+  __shared__ u32x4 ws0[WSLAB / 16], ws1[WSLAB / 16], ws2[NST > 2 ? WSLAB / 16 : 1], ws3[NST > 3 ? WSLAB / 16 : 1];
   auto abuf = [&](int s) __attribute__((always_inline)) -> char* {
     return reinterpret_cast<char*>(s == 0 ? as0 : s == 1 ? as1 : s == 2 ? as2 : as3);
   };
   auto wbuf = [&](int s) __attribute__((always_inline)) -> char* {
     return reinterpret_cast<char*>(s == 0 ? ws0 : s == 1 ? ws1 : s == 2 ? ws2 : ws3);
   };
+  // chunk c of slab row r sits at physical chunk c ^ swz(r): the 16-byte
+  // fragment reads of 16 consecutive rows then cover all 64 banks once
+  auto swz = [](int r) __attribute__((always_inline)) { return (r / RPL) & (CPR - 1); };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;  // this wave's 64 x 64 quarter
+  const int wm = wave % WGM, wn = wave / WGM;  // this wave's part of the tile
 
   // tile of this work-group: groups of kGroupM tile rows, column-major inside
   const int t = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
@@ -142,113 +191,169 @@ __global__ __launch_bounds__(256, 2) void gemm_bias_gelu_kernel(GemmParams p) {
   const int gsize = min(kGroupM, p.tiles_m - first_m);
   const int tm = first_m + (t - group * per_group) % gsize;
   const int tn = (t - group * per_group) / gsize;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int m0 = tm * BM, n0 = tn * BN;
 
   // buffer resources over the work-group's rows of A and W (rows past M or N
   // are outside the range)
-  const uint32_t rowb = (uint32_t)p.K * 2u;
+  const uint32_t rowg = (uint32_t)p.K * 2u;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.a + (size_t)m0 * p.K), (short)0, (uint32_t)min(kBM, p.M - m0) * rowb, kBufferWord3);
+      (void*)(p.a + (size_t)m0 * p.K), (short)0, (uint32_t)min(BM, p.M - m0) * rowg, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.w + (size_t)n0 * p.K), (short)0, (uint32_t)min(kBN, p.N - n0) * rowb, kBufferWord3);
+      (void*)(p.w + (size_t)n0 * p.K), (short)0, (uint32_t)min(BN, p.N - n0) * rowg, kBufferWord3);
 
   // load slots: instruction i of this wave fills 1 KiB block i*4 + wave of a
-  // slab; lane l writes its bytes 16l..16l+15, that is row (slot / 4),
-  // physical chunk slot % 4, holding logical chunk pc ^ ((row >> 2) & 3)
-  uint32_t lrow[NLD];
-  int lk[NLD];
+  // slab; lane l writes bytes 16l..16l+15 of it: row slot / CPR, physical
+  // chunk slot % CPR, which holds logical chunk pc ^ swz(row)
+  uint32_t arow[NLA], wrow[NLW];
+  int ak[NLA], wk[NLW];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
+  for (int i = 0; i < NLA; ++i) {
     const int slot = (i * kWaves + wave) * 64 + lane;
-    const int row = slot >> 2, pc = slot & 3;
-    const int c = pc ^ ((row >> 2) & 3);
-    lrow[i] = (uint32_t)row * rowb;
-    lk[i] = c * 8;
+    const int row = slot / CPR;
+    arow[i] = (uint32_t)row * rowg;
+    ak[i] = ((slot % CPR) ^ swz(row)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < NLW; ++i) {
+    const int slot = (i * kWaves + wave) * 64 + lane;
+    const int row = slot / CPR;
+    wrow[i] = (uint32_t)row * rowg;
+    wk[i] = ((slot % CPR) ^ swz(row)) * 8;
   }
   auto issue = [&](int slab, int stage) __attribute__((always_inline)) {
-    const int k0 = slab * kBK;
+    const int k0 = slab * BK;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int k = k0 + lk[i];
-      const uint32_t off = k < p.K ? lrow[i] + (uint32_t)k * 2u : kOutOfRange;
+    for (int i = 0; i < NLA; ++i) {
+      const int k = k0 + ak[i];
+      const uint32_t off = k < p.K ? arow[i] + (uint32_t)k * 2u : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(abuf(stage) + (i * kWaves + wave) * 1024), 16, off,
                                                0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int k = k0 + lk[i];
-      const uint32_t off = k < p.K ? lrow[i] + (uint32_t)k * 2u : kOutOfRange;
+    for (int i = 0; i < NLW; ++i) {
+      const int k = k0 + wk[i];
+      const uint32_t off = k < p.K ? wrow[i] + (uint32_t)k * 2u : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(wbuf(stage) + (i * kWaves + wave) * 1024), 16, off,
                                                0, 0, 0);
     }
   };
 
-  // fragment reads: block b (32 rows) of the wave's quarter, k-step s (16
-  // wide) of the slab; lane l reads row 32b + l%32, logical chunk 2s + l/32
+  // fragment of block row0.. (32 rows), k-step s (16 wide) of a slab: lane l
+  // reads row row0 + l%32, logical chunk 2s + l/32
   const int fr = lane & 31, fh = lane >> 5;
   auto frag = [&](const char* base, int row0, int s) __attribute__((always_inline)) -> u32x4 {
     const int r = row0 + fr;
-    const int pc = (2 * s + fh) ^ ((r >> 2) & 3);
-    return *reinterpret_cast<const u32x4*>(base + r * (kBK * 2) + pc * 16);
+    const int pc = (2 * s + fh) ^ swz(r);
+    return *reinterpret_cast<const u32x4*>(base + r * ROWB + pc * 16);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[WTN][WTM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WTN; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WTM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (p.K + kBK - 1) / kBK;
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  for (int j = 0; j < nk; ++j) {
-    const int st = j & 3;
-    // slab j has landed once at most the two later slabs' loads are in
-    // flight; the barrier makes every wave's part of it visible, and tells
-    // that every wave has finished reading stage (j+3)%4 (slab j-1, whose
-    // fragments were all consumed by the previous step's products)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(4 * NLD) : "memory");
-    issue(j + 3, (j + 3) & 3);
-    const char* at = abuf(st);
-    const char* wt = wbuf(st);
+  // the fragments of k-step 0 of the next slab, read at the end of a step
+  u32x4 wpre[WTN], apre[WTM];
+  auto read_pre = [&](int stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      u32x4 wf[2], af[2];
+    for (int b = 0; b < WTN; ++b) wpre[b] = frag(wbuf(stage), wn * 32 * WTN + b * 32, 0);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        wf[b] = frag(wt, wn * 64 + b * 32, s);
-        af[b] = frag(at, wm * 64 + b * 32, s);
-      }
+    for (int b = 0; b < WTM; ++b) apre[b] = frag(abuf(stage), wm * 32 * WTM + b * 32, 0);
+  };
+
+  // step j (slab j in stage j % NST, passed at compile time as ST)
+  auto step = [&](int j, auto st_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_tag)::value;
+    // slabs j and j+1 have landed once at most the NST-3 later slabs' loads
+    // are in flight; the barrier makes every wave's part of them visible
+    // (slab j+1 is read at the end of this step), and tells that every wave
+    // has finished reading the stage of slab j-1 (its fragments were all
+    // consumed by the previous steps' products), which slab j+NST-1 now
+    // overwrites.  Slabs past the end are zeros and may be read.
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 3) * (NLA + NLW)) : "memory");
+    issue(j + NST - 1, (ST + NST - 1) % NST);
+    const char* at = abuf(ST);
+    const char* wt = wbuf(ST);
+    u32x4 wf[BK / 16][WTN], af[BK / 16][WTM];
 #pragma unroll
-      for (int bn = 0; bn < 2; ++bn)
+    for (int b = 0; b < WTN; ++b) wf[0][b] = wpre[b];
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm) acc[bn][bm] = mfma_32x32x16<BF16>(wf[bn], af[bm], acc[bn][bm]);
+    for (int b = 0; b < WTM; ++b) af[0][b] = apre[b];
+#pragma unroll
+    for (int s = 1; s < BK / 16; ++s) {
+#pragma unroll
+      for (int b = 0; b < WTN; ++b) wf[s][b] = frag(wt, wn * 32 * WTN + b * 32, s);
+#pragma unroll
+      for (int b = 0; b < WTM; ++b) af[s][b] = frag(at, wm * 32 * WTM + b * 32, s);
     }
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s)
+#pragma unroll
+      for (int bn = 0; bn < WTN; ++bn)
+#pragma unroll
+        for (int bm = 0; bm < WTM; ++bm) acc[bn][bm] = mfma_32x32x16<BF16>(wf[s][bn], af[s][bm], acc[bn][bm]);
+    read_pre((ST + 1) % NST);
+  };
+
+  const int nk = (p.K + BK - 1) / BK;
+  static_for<0, NST - 1>([&](auto it) { issue(it.value, it.value); });
+
+  // the bias of the lane's columns n0 + 32(WTN wn + bn) + 8g + 4(l/32) + 0..3,
+  // read before the loop (8-byte loads where aligned and inside N)
+  u32x2 bias_pk[WTN][4];
+  {
+    const bool bvec = ((uintptr_t)p.bias & 7u) == 0;
+#pragma unroll
+    for (int bn = 0; bn < WTN; ++bn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nb = n0 + (wn * WTN + bn) * 32 + 8 * g + 4 * fh;
+        u32x2 v = {0u, 0u};
+        if (p.bias) {
+          if (bvec && nb + 3 < p.N) {
+            v = *reinterpret_cast<const u32x2*>(p.bias + nb);
+          } else {
+            uint16_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = nb + e < p.N ? p.bias[nb + e] : (uint16_t)0;
+            v[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+            v[1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+          }
+        }
+        bias_pk[bn][g] = v;
+      }
   }
+  // slab 0 has landed once the NST-2 later slabs' loads are in flight
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 2) * (NLA + NLW)) : "memory");
+  read_pre(0);
+  int j = 0;
+  for (; j + NST <= nk; j += NST) static_for<0, NST>([&](auto it) { step(j + it.value, it); });
+  static_for<0, NST - 1>([&](auto it) {
+    if (j + it.value < nk) step(j + it.value, it);
+  });
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // epilogue: lane holds C[m][n] for m = m0 + 64wm + 32bm + l%32 and
-  // n = n0 + 64wn + 32bn + 8g + 4(l/32) + e (accumulator slot 4g + e)
+  // epilogue: lane holds C[m][n] for m = m0 + 32(WTM wm + bm) + l%32 and
+  // n = n0 + 32(WTN wn + bn) + 8g + 4(l/32) + e (accumulator slot 4g + e)
   const bool vec = (p.N & 3) == 0;
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm) {
-    const int m = m0 + wm * 64 + bm * 32 + fr;
+  for (int bm = 0; bm < WTM; ++bm) {
+    const int m = m0 + (wm * WTM + bm) * 32 + fr;
     if (m >= p.M) continue;
     uint16_t* crow = p.c + (size_t)m * p.N;
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn)
+    for (int bn = 0; bn < WTN; ++bn)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int nb = n0 + wn * 64 + bn * 32 + 8 * g + 4 * fh;
+        const int nb = n0 + (wn * WTN + bn) * 32 + 8 * g + 4 * fh;
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int n = nb + e;
-          const float bv = (p.bias && n < p.N) ? to_f32<BF16>(p.bias[n]) : 0.f;
-          y[e] = gelu(acc[bn][bm][4 * g + e] + bv);
+          const uint16_t bh = (uint16_t)(bias_pk[bn][g][e >> 1] >> (16 * (e & 1)));
+          y[e] = gelu(acc[bn][bm][4 * g + e] + to_f32<BF16>(bh));
         }
         if (vec && nb + 3 < p.N) {
           u32x2 v;
@@ -281,10 +386,10 @@ extern "C" fa_status gemm_bias_gelu(const void* a, const void* w, const void* bi
   if (K % 8 != 0) return FA_ERR_UNSUPPORTED;
   const int64_t lim = (int64_t)1 << 31;
   if (M >= lim || N >= lim || K >= lim) return FA_ERR_INVALID_ARG;
-  // a work-group's buffer range, 128 rows of 2K bytes, and the tile count
-  // stay inside 32 bits
-  if ((int64_t)kBM * K * 2 >= (int64_t)kOutOfRange) return FA_ERR_INVALID_ARG;
-  const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+  // a work-group's buffer range (up to 256 rows of 2K bytes) and the tile
+  // count stay inside 32 bits
+  if ((int64_t)256 * K * 2 >= (int64_t)kOutOfRange) return FA_ERR_INVALID_ARG;
+  const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM, tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
   if (tiles_m * tiles_n >= lim) return FA_ERR_INVALID_ARG;
   const size_t a_bytes = (size_t)M * (size_t)K * 2, w_bytes = (size_t)N * (size_t)K * 2;
   const size_t c_bytes = (size_t)M * (size_t)N * 2, b_bytes = (size_t)N * 2;
@@ -303,9 +408,13 @@ extern "C" fa_status gemm_bias_gelu(const void* a, const void* w, const void* bi
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   void* args[] = {&p};
-  const void* fn = dtype == FA_BF16 ? reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<true>)
-                                    : reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<false>);
-  const hipError_t err = hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kWaves), args, 0,
+  const void* fn =
+      dtype == FA_BF16
+          ? reinterpret_cast<const void*>(
+                &gemm_bias_gelu_kernel<true, Cfg::WGN, Cfg::WGM, Cfg::WTN, Cfg::WTM, Cfg::BK, Cfg::NST>)
+          : reinterpret_cast<const void*>(
+                &gemm_bias_gelu_kernel<false, Cfg::WGN, Cfg::WGM, Cfg::WTN, Cfg::WTM, Cfg::BK, Cfg::NST>);
+  const hipError_t err = hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * Cfg::NW), args, 0,
                                          static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
