@@ -40,7 +40,7 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 _MASK64 = (1 << 64) - 1
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "a": 3, "w": 4, "bias": 5}  # attention; GEMM + bias + GELU
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "a": 3, "w": 4, "bias": 5, "x": 6, "g": 7}  # attention; GEMM; row-wise
 DTYPES = ("f16", "bf16")
 
 

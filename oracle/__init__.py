@@ -33,14 +33,16 @@ DTYPE_CODE = {"f16": 0, "bf16": 1}
 
 def build() -> str:
     """Compile the oracles with gcc (plain -O2, no fast-math, no FP contraction):
-    the attention oracle here and the GEMM + bias + GELU oracle of ``oracle.gemm``."""
+    the attention oracle here, the GEMM + bias + GELU oracle of ``oracle.gemm``
+    and the row-wise (softmax, RMSNorm + SiLU) oracles of ``oracle.rowwise``."""
     cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
            "-std=c11", "-Wall", "-Wextra", _SRC, "-o", _LIB + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
-    from . import gemm
+    from . import gemm, rowwise
 
     gemm.build()
+    rowwise.build()
     return _LIB
 
 
