@@ -44,6 +44,7 @@ PEAK_TFLOPS_F16 = 2516.6
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "tile_level_programming_amd", "csrc", "fa_fwd.hip")
 GEMM_SRC = os.path.join(ROOT, "tile_level_programming_amd", "csrc", "gemm_bias_gelu.hip")
+ROWWISE_SRC = os.path.join(ROOT, "tile_level_programming_amd", "csrc", "rowwise.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -226,12 +227,109 @@ def run_gemm(args, w):
     print(json.dumps(line), flush=True)
 
 
+def run_rows(args, w):
+    """One step = one row_softmax or rmsnorm_silu call over the workload's rows."""
+    import torch
+
+    import oracle.rowwise as orw
+    from tile_level_programming_amd import fa
+
+    log(f"[bench] workload {w.name}: generating seeded inputs")
+    x, g = fi.make_row_inputs(w)
+    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    xd = torch.from_numpy(x.view(np.int16)).view(tdt).to(dev)
+    gd = torch.from_numpy(g.view(np.int16)).view(tdt).to(dev) if g is not None else None
+    y = torch.empty_like(xd)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    dt_code = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
+
+    def step():
+        if w.op == "softmax":
+            st = fa.row_softmax(xd.data_ptr(), y.data_ptr(), w.R, w.C, dt_code, sp)
+        else:
+            st = fa.rmsnorm_silu(xd.data_ptr(), gd.data_ptr(), y.data_ptr(), w.R, w.C, w.eps, dt_code, sp)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start.record(stream)
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms_kernel = float(np.mean(launch_ms))
+    nbytes = w.io_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    gbs_kernel = nbytes / (ms_kernel * 1e-3) / 1e9
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {gbs:.0f} GB/s; per launch mean {ms_kernel:.4f} ms "
+        f"(min {min(launch_ms):.4f}, max {max(launch_ms):.4f}), {gbs_kernel:.0f} GB/s")
+
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, w.R - 1], rng.integers(0, w.R, 62)]))
+    ys = y[torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+    threads = min(16, os.cpu_count() or 1)
+    ref = (orw.softmax_rows(x, w.dtype, rows=rows, threads=threads) if w.op == "softmax"
+           else orw.rmsnorm_silu_rows(x, g, w.dtype, w.eps, rows=rows, threads=threads))
+    rel = 2.0 ** -10 if w.dtype == "f16" else 2.0 ** -7
+    floor = (2.0 ** -24 if w.dtype == "f16" else 1e-30) if w.op == "softmax" else 1e-5
+    over = float((np.abs(ys - ref) - (rel * np.abs(ref) + floor)).max())
+    parity_ok = bool(over <= 0 and np.isfinite(ys).all())
+    log(f"[bench] sampled parity: max (|dy| - bar) = {over:.2e} ok={parity_ok}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = min(w.R, max(threads, int(args.cpu_seconds * 2e8 / (w.C * 20))))
+        rws = rng.integers(0, w.R, n)
+        t0 = time.perf_counter()
+        if w.op == "softmax":
+            orw.softmax_rows(x, w.dtype, rows=rws, threads=threads)
+        else:
+            orw.rmsnorm_silu_rows(x, g, w.dtype, w.eps, rows=rws, threads=threads)
+        dtc = time.perf_counter() - t0
+        cpu = {"value": round(n * w.C * 4 / dtc / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n} seeded random rows of {w.name} ({n / w.R:.2%}), float64, {dtc:.2f} s wall"}
+    line = {
+        "metric": f"{w.op} GB/s of algorithmic bytes and % of MI355X HBM peak",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded i.i.d. normal rows" + (", normal weight)" if g is not None else ")"),
+        "config": {"workload": w.name, "op": w.op, "R": w.R, "C": w.C, "algorithmic_bytes": nbytes,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs_kernel, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs_kernel / PEAK_HBM_GBS, 4), "traffic": traffic_for(w.name, ROWWISE_SRC),
+                     "kernel_ms": round(ms_kernel, 5), "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+        "parity_sample": {"rows": int(rows.size), "max_excess_over_bar": over, "ok": parity_ok},
+        "kernel_sha256_16": kernel_hash(ROWWISE_SRC),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=fi.HEADLINE, choices=list(fi.ALL_WORKLOADS) + list(fi.GEMM_WORKLOADS))
+    ap.add_argument("--workload", default=fi.HEADLINE, choices=list(fi.ALL_WORKLOADS) + list(fi.GEMM_WORKLOADS)
+                    + list(fi.ROW_WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -261,6 +359,9 @@ def main():
 
     if args.workload in fi.GEMM_WORKLOADS:
         run_gemm(args, fi.GEMM_WORKLOADS[args.workload])
+        return
+    if args.workload in fi.ROW_WORKLOADS:
+        run_rows(args, fi.ROW_WORKLOADS[args.workload])
         return
     w = fi.ALL_WORKLOADS[args.workload]
     log(f"[bench] workload {w.name}: generating seeded inputs")

@@ -206,6 +206,45 @@ def make_gemm_inputs(w: GemmWorkload):
     return a, wt, b
 
 
+@dataclasses.dataclass(frozen=True)
+class RowWorkload:
+    """A row-wise kernel on R rows of length C: op "softmax" (x ~ N(0, sigma^2))
+    or "rmsnorm_silu" (x ~ N(0, sigma^2), weight g ~ N(0, 1), eps 1e-6)."""
+    name: str
+    op: str
+    R: int
+    C: int
+    dtype: str
+    seed: int
+    sigma: float = 1.0
+    eps: float = 1e-6
+
+    def io_bytes(self) -> int:
+        """x read once, y written once (and g read once)."""
+        return 2 * 2 * self.R * self.C + (2 * self.C if self.op == "rmsnorm_silu" else 0)
+
+
+def make_row_inputs(w: RowWorkload):
+    """(x, g or None) uint16 bit-pattern arrays for a row-wise workload."""
+    x = tensor_bits(w.seed, "x", (w.R, w.C), w.dtype, w.sigma)
+    g = tensor_bits(w.seed, "g", (w.C,), w.dtype) if w.op == "rmsnorm_silu" else None
+    return x, g
+
+
+# Row-wise kernels.  The pages give no shapes; these are attention-score rows
+# (4096 keys) and vocabulary-size rows (32000) for the softmax, and a VAE
+# feature map (65536 positions x 512 channels) and transformer hidden states
+# (16384 x 4096) for RMSNorm + SiLU.
+ROW_WORKLOADS = {
+    "softmax_r32768_c4096_f16": RowWorkload("softmax_r32768_c4096_f16", "softmax", 32768, 4096, "f16", 10, 3.0),
+    "softmax_r8192_c32000_bf16": RowWorkload("softmax_r8192_c32000_bf16", "softmax", 8192, 32000, "bf16", 11, 3.0),
+    "rmsnorm_silu_r65536_c512_bf16": RowWorkload("rmsnorm_silu_r65536_c512_bf16", "rmsnorm_silu", 65536, 512,
+                                                 "bf16", 12),
+    "rmsnorm_silu_r16384_c4096_f16": RowWorkload("rmsnorm_silu_r16384_c4096_f16", "rmsnorm_silu", 16384, 4096,
+                                                 "f16", 13),
+}
+
+
 # GEMM with the fused bias + GELU epilogue.  The pages name no shapes (their
 # example tile is 128 x 128 x 32); these are the up-projection of a
 # transformer MLP (8192 tokens, 4096 -> 16384) and a square one.

@@ -30,7 +30,8 @@ def fa():
 
 def test_header_declares_entry_points():
     assert _declared_functions() == ["fa_fwd", "fa_fwd_split", "fa_fwd_split_count", "fa_fwd_split_workspace_size",
-                                     "fa_lse_merge", "fa_status_string", "gemm_bias_gelu"]
+                                     "fa_lse_merge", "fa_status_string", "gemm_bias_gelu", "rmsnorm_silu",
+                                     "row_softmax"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -184,4 +185,30 @@ def test_gemm_invalid_arguments(fa, kw):
 @pytest.mark.parametrize("kw", [dict(K=12), dict(K=100), dict(dtype=3)])
 def test_gemm_unsupported(fa, kw):
     assert _call_gemm(fa, **kw) == fa.FA_ERR_UNSUPPORTED
+
+
+# --- row-wise kernels: host-side checks ----------------------------------------
+
+
+@pytest.mark.parametrize("kw", [dict(x=0), dict(y=0), dict(x=A + 1), dict(y=2 * A + 3), dict(R=0), dict(C=0),
+                                dict(R=1 << 31), dict(y=A + 64)])
+def test_row_softmax_invalid(fa, kw):
+    args = dict(x=A, y=2 * A, R=100, C=500, dtype=fa.FA_F16, stream=0)
+    args.update(kw)
+    assert fa.row_softmax(**args) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(C=32769), dict(dtype=2)])
+def test_row_softmax_unsupported(fa, kw):
+    args = dict(x=A, y=2 * A, R=100, C=500, dtype=fa.FA_F16, stream=0)
+    args.update(kw)
+    assert fa.row_softmax(**args) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(g=0), dict(g=3 * A + 1), dict(eps=-1.0), dict(eps=float("nan")),
+                                dict(eps=float("inf")), dict(g=2 * A + 64), dict(x=0)])
+def test_rmsnorm_silu_invalid(fa, kw):
+    args = dict(x=A, g=3 * A, y=2 * A, R=100, C=500, eps=1e-6, dtype=fa.FA_BF16, stream=0)
+    args.update(kw)
+    assert fa.rmsnorm_silu(**args) == fa.FA_ERR_INVALID_ARG
 

@@ -1,0 +1,149 @@
+"""GPU parity of the row-wise kernels (row_softmax, rmsnorm_silu) against the
+float64 oracles, through the C ABI.
+
+Bar, from the arithmetic: fp32 inside, one rounding to the output type, so
+the error is half an ulp of the output plus fp32 errors.  |y - y_ref| <=
+rel |y_ref| + floor with rel = 2^-10 (fp16) or 2^-7 (bf16) (one ulp) and a
+floor below any normal output: 2^-24 for fp16 softmax (the subnormal
+spacing), 1e-5 for RMSNorm + SiLU (fp32 errors of O(1) intermediates).
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+
+pytestmark = pytest.mark.gpu
+
+REL = {"f16": 2.0 ** -10, "bf16": 2.0 ** -7}
+FLOOR = {("softmax", "f16"): 2.0 ** -24, ("softmax", "bf16"): 1e-30, ("rmsnorm_silu", "f16"): 1e-5,
+         ("rmsnorm_silu", "bf16"): 1e-5}
+THREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def fa():
+    from tile_level_programming_amd import fa as mod
+
+    return mod
+
+
+@pytest.fixture(scope="module")
+def ro():
+    import oracle.rowwise as r
+
+    r._load()
+    return r
+
+
+def to_dev(torch, bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16).cuda()
+
+
+def check(y, ref, op, dtype, what):
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    err = np.abs(y - ref) - (REL[dtype] * np.abs(ref) + FLOOR[(op, dtype)])
+    i = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= 0, f"{what}: over the bar by {err.max():.3e} at {i}: {y[i]} vs {ref[i]}"
+
+
+def run(torch, fa, op, x, g, dtype, eps=1e-6, offset=0, guard=4096):
+    R, C = x.shape
+    xd = to_dev(torch, x, dtype)
+    buf = torch.full((guard + R * C + guard,), float("nan"), dtype=xd.dtype, device="cuda")
+    lo, hi = guard + offset, guard + offset + R * C  # offset 1: an unaligned output, the element path
+    y = buf[lo:hi].view(R, C)
+    dt = fa.FA_F16 if dtype == "f16" else fa.FA_BF16
+    s = torch.cuda.current_stream().cuda_stream
+    if op == "softmax":
+        st = fa.row_softmax(xd.data_ptr(), y.data_ptr(), R, C, dt, s)
+    else:
+        gd = to_dev(torch, g, dtype)
+        st = fa.rmsnorm_silu(xd.data_ptr(), gd.data_ptr(), y.data_ptr(), R, C, eps, dt, s)
+    assert st == fa.FA_OK, fa.fa_status_string(st)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(buf[:lo]).all()) and bool(torch.isnan(buf[hi:]).all()), "guard overwritten"
+    return y.float().double().cpu().numpy()
+
+
+SHAPES = [(1, 1), (3, 7), (5, 64), (9, 100), (17, 512), (33, 520), (4, 2048), (7, 2049), (3, 4096), (2, 8000),
+          (5, 16384), (2, 30001), (2, 32768)]
+
+
+@pytest.mark.parametrize("op", ["softmax", "rmsnorm_silu"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"r{s[0]}_c{s[1]}")
+def test_rowwise_parity(torch_dev, fa, ro, op, dtype, shape):
+    R, C = shape
+    w = fi.RowWorkload("t", op, R, C, dtype, 81, 3.0 if op == "softmax" else 1.0)
+    x, g = fi.make_row_inputs(w)
+    y = run(torch_dev, fa, op, x, g, dtype)
+    ref = ro.softmax_rows(x, dtype, threads=THREADS) if op == "softmax" else \
+        ro.rmsnorm_silu_rows(x, g, dtype, w.eps, threads=THREADS)
+    check(y, ref, op, dtype, f"{op} {shape} {dtype}")
+
+
+@pytest.mark.parametrize("op", ["softmax", "rmsnorm_silu"])
+def test_rowwise_unaligned_output(torch_dev, fa, ro, op):
+    dtype = "bf16"
+    w = fi.RowWorkload("t", op, 40, 96, dtype, 82)
+    x, g = fi.make_row_inputs(w)
+    y = run(torch_dev, fa, op, x, g, dtype, offset=1)
+    ref = ro.softmax_rows(x, dtype) if op == "softmax" else ro.rmsnorm_silu_rows(x, g, dtype, w.eps)
+    check(y, ref, op, dtype, f"{op} unaligned")
+
+
+def test_softmax_extremes(torch_dev, fa, ro):
+    dtype = "f16"
+    x = np.zeros((4, 300), np.float32)
+    x[0] = 60000.0                          # constant, huge
+    x[1, 7] = 50.0                          # one dominant entry
+    x[2] = np.linspace(-60000, 60000, 300)  # wide range
+    x[3] = -65504.0
+    bits = fi.f32_to_bits(x, dtype)
+    y = run(torch_dev, fa, "softmax", bits, None, dtype)
+    check(y, ro.softmax_rows(bits, dtype), "softmax", dtype, "extremes")
+
+
+def test_rmsnorm_silu_eps_and_zero_rows(torch_dev, fa, ro):
+    dtype = "f16"
+    w = fi.RowWorkload("t", "rmsnorm_silu", 6, 256, dtype, 83)
+    x, g = fi.make_row_inputs(w)
+    x[2] = 0                                 # a zero row: y = silu(0) = 0
+    for eps in (0.0, 1e-6, 0.5):
+        if eps == 0.0:
+            xs = x[[0, 1, 3, 4, 5]]           # eps 0 on a zero row is 0/0
+        else:
+            xs = x
+        y = run(torch_dev, fa, "rmsnorm_silu", xs, g, dtype, eps)
+        check(y, ro.rmsnorm_silu_rows(xs, g, dtype, eps), "rmsnorm_silu", dtype, f"eps {eps}")
+
+
+@pytest.mark.parametrize("name", list(fi.ROW_WORKLOADS))
+def test_row_workload_parity(torch_dev, fa, ro, name):
+    # the benchmarked shapes at full size, on sampled rows
+    torch = torch_dev
+    w = fi.ROW_WORKLOADS[name]
+    print(f"[rowwise] workload {name}", flush=True)
+    x, g = fi.make_row_inputs(w)
+    xd = to_dev(torch, x, w.dtype)
+    y = fa.softmax(xd) if w.op == "softmax" else fa.rmsnorm_silu_rows(xd, to_dev(torch, g, w.dtype), w.eps)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, w.R - 1], rng.integers(0, w.R, 62)]))
+    ys = y[torch.from_numpy(rows).cuda()].float().double().cpu().numpy()
+    ref = ro.softmax_rows(x, w.dtype, rows=rows, threads=THREADS) if w.op == "softmax" else \
+        ro.rmsnorm_silu_rows(x, g, w.dtype, w.eps, rows=rows, threads=THREADS)
+    check(ys, ref, w.op, w.dtype, name)

@@ -1,8 +1,8 @@
 """Compile the HIP library for gfx950, in-tree.
 
-The library is two HIP translation units (attention; GEMM with a fused bias +
-GELU epilogue) with the C ABI declared in ``include/fa.h`` and
-``include/gemm.h``; it is built with hipcc for gfx950 only, with packed fp32
+The library is three HIP translation units (attention; GEMM with a fused bias
++ GELU epilogue; row softmax and RMSNorm + SiLU) with the C ABI declared in
+``include/fa.h``, ``include/gemm.h`` and ``include/rowwise.h``; it is built with hipcc for gfx950 only, with packed fp32
 instructions disabled in device code.
 """
 
@@ -15,7 +15,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
-SRCS = [SRC, os.path.join(PKG, "csrc", "gemm_bias_gelu.hip")]
+SRCS = [SRC, os.path.join(PKG, "csrc", "gemm_bias_gelu.hip"), os.path.join(PKG, "csrc", "rowwise.hip")]
 LIB = os.path.join(PKG, "libfa_mi355x.so")
 ARCH = "gfx950"
 

@@ -1,8 +1,9 @@
-"""ctypes binding of the C ABI in include/fa.h and include/gemm.h (argument
-marshalling only).
+"""ctypes binding of the C ABI in include/fa.h, include/gemm.h and
+include/rowwise.h (argument marshalling only).
 
-Every step of the attention forward pass and of the GEMM with its fused
-bias + GELU epilogue runs in the HIP library ``libfa_mi355x.so``; this module
+Every step of the attention forward pass, of the GEMM with its fused
+bias + GELU epilogue and of the row-wise kernels runs in the HIP library
+``libfa_mi355x.so``; this module
 only loads it, converts arguments and, in the torch-level helpers, allocates
 outputs (and the split workspace) with torch.  There is no fallback: if the
 library is missing, importing the binding raises.
@@ -59,6 +60,12 @@ def _load():
     lib.gemm_bias_gelu.restype = ctypes.c_int
     lib.gemm_bias_gelu.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.row_softmax.restype = ctypes.c_int
+    lib.row_softmax.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                ctypes.c_void_p]
+    lib.rmsnorm_silu.restype = ctypes.c_int
+    lib.rmsnorm_silu.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -123,6 +130,46 @@ def linear_gelu(a, w, bias=None, out=None):
     if st != FA_OK:
         raise FaError(st)
     return out
+
+
+def row_softmax(x: int, y: int, R: int, C: int, dtype: int, stream: int) -> int:
+    """Direct call of the C entry point with raw device addresses; returns the status."""
+    return int(_lib.row_softmax(x, y, R, C, int(dtype), stream))
+
+
+def rmsnorm_silu(x: int, g: int, y: int, R: int, C: int, eps: float, dtype: int, stream: int) -> int:
+    """Direct call of the C entry point with raw device addresses; returns the status."""
+    return int(_lib.rmsnorm_silu(x, g, y, R, C, float(eps), int(dtype), stream))
+
+
+def _rows_call(x, extra, fn, out):
+    import torch
+
+    if x.dtype not in (torch.float16, torch.bfloat16) or x.dim() != 2:
+        raise TypeError("x must be a [R, C] float16 or bfloat16 tensor")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    dt = FA_F16 if x.dtype == torch.float16 else FA_BF16
+    st = fn(x, out, dt, torch.cuda.current_stream(x.device).cuda_stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return out
+
+
+def softmax(x, out=None):
+    """Row softmax of a [R, C] device tensor (row_softmax); returns y like x."""
+    return _rows_call(x, None, lambda t, o, dt, s: row_softmax(t.data_ptr(), o.data_ptr(), t.shape[0], t.shape[1],
+                                                               dt, s), out)
+
+
+def rmsnorm_silu_rows(x, g, eps: float = 1e-6, out=None):
+    """silu(x / rms(x) * g) along the rows of a [R, C] device tensor; g [C]."""
+    if g.dtype != x.dtype or tuple(g.shape) != (x.shape[1],) or not g.is_contiguous():
+        raise ValueError("g must be a contiguous [C] tensor of x's dtype")
+    return _rows_call(x, g, lambda t, o, dt, s: rmsnorm_silu(t.data_ptr(), g.data_ptr(), o.data_ptr(), t.shape[0],
+                                                             t.shape[1], eps, dt, s), out)
 
 
 def split_count(B: int, H: int, Sq: int, Sk: int, n_split: int = 0) -> int:
