@@ -28,8 +28,10 @@
 //    global 16-byte chunk that belongs at its LDS slot, which lays a row's
 //    four chunks out XOR-swizzled (chunk c of row r at c ^ ((r >> 2) & 3)):
 //    the fragment reads of 16 consecutive rows then hit all 64 banks once.
-//    The first k-step's fragments of the next slab are read at the end of
-//    each step, so a step's products start without waiting for LDS.
+//    The first k-step's fragments of the next slab are read during each
+//    step, between its last products, so a step's products start without
+//    waiting for LDS; a step issues its loads, then its remaining fragment
+//    reads, then its products.
 //  * Rows past M or N lie outside the buffer range and read as zeros;
 //    chunks past K get an offset outside the range and read as zeros.
 //    Slabs past the end are loaded as zeros too, so every wait has a fixed
@@ -61,6 +63,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // a buffer offset past any range: reads zeros
 constexpr int kGroupM = 4;                      // tile rows per ordering group
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 // Tile configuration: a work-group of WGN x WGM waves (n x m), each wave
 // owning WTN x WTM blocks of 32 x 32; K is streamed in BK-wide slabs through
@@ -275,6 +280,8 @@ __global__ __launch_bounds__(64 * WGN * WGM) void gemm_bias_gelu_kernel(GemmPara
     // overwrites.  Slabs past the end are zeros and may be read.
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 3) * (NLA + NLW)) : "memory");
     issue(j + NST - 1, (ST + NST - 1) % NST);
+    // the loads go out first: nothing of the step may be scheduled above them
+    __builtin_amdgcn_sched_barrier(0);
     const char* at = abuf(ST);
     const char* wt = wbuf(ST);
     u32x4 wf[BK / 16][WTN], af[BK / 16][WTM];
@@ -296,6 +303,18 @@ __global__ __launch_bounds__(64 * WGN * WGM) void gemm_bias_gelu_kernel(GemmPara
 #pragma unroll
         for (int bm = 0; bm < WTM; ++bm) acc[bn][bm] = mfma_32x32x16<BF16>(wf[s][bn], af[s][bm], acc[bn][bm]);
     read_pre((ST + 1) % NST);
+    // the fragments of the later k-steps first, then the k-step-0 products,
+    // then the later products with the next slab's first fragments read
+    // between them (measured: +11% on 8192 x 16384 x 4096)
+    constexpr int NF = WTN + WTM, NM = WTN * WTM;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NF * (BK / 16 - 1), 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, NM, 0);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, NM * (BK / 16 - 1) - NF, 0);
   };
 
   const int nk = (p.K + BK - 1) / BK;
