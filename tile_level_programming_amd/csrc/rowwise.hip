@@ -12,8 +12,9 @@
 //     RMSNorm + SiLU: z_j = x_j / sqrt(mean_j x_j^2 + eps) * g_j,  y_j = z_j / (1 + exp(-z_j))
 //
 // Both read a row once and write it once, so they are bound by HBM.  A row
-// is held in registers by a group of TPR threads (one wave for rows up to
-// 2048 elements, the whole 256-thread work-group beyond), each thread
+// is held in registers by a group of TPR threads (16, 32 or 64 lanes of a
+// wave for rows up to 2048 elements, several rows per wave for short rows;
+// the whole 256-thread work-group beyond), each thread
 // holding CPT chunks of 8 elements loaded with 16-byte loads (element loads
 // when the row length is not a multiple of 8).  The reductions run within
 // the wave by lane exchanges and, for 256-thread groups, across its four
@@ -67,12 +68,12 @@ __device__ __forceinline__ float elem(const u32x4& v, int e) {
   return (e & 1) ? hi16<BF16>(v[e >> 1]) : lo16<BF16>(v[e >> 1]);
 }
 
-// reductions over the TPR threads of a row group (TPR = 64: one wave; 256:
-// the work-group, through LDS)
+// reductions over the TPR threads of a row group (TPR = 16, 32 or 64:
+// lanes of one wave; 256: the work-group, through LDS)
 template <int TPR, bool MAX>
 __device__ __forceinline__ float group_reduce(float x, float* red) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
+  for (int o = (TPR < 64 ? TPR : 64) / 2; o >= 1; o >>= 1) {
     const float y = __shfl_xor(x, o, 64);
     x = MAX ? __builtin_elementwise_maximum(x, y) : x + y;
   }
@@ -216,9 +217,13 @@ hipError_t launch3(const uint16_t* x, const uint16_t* g, uint16_t* y, int R, int
 template <bool BF16, int OP>
 hipError_t launch2(const uint16_t* x, const uint16_t* g, uint16_t* y, int R, int C, float eps, bool vec,
                    hipStream_t s) {
+  // short rows: a few rows per wave, so that each thread has up to four
+  // 16-byte loads in flight
   const int chunks = (C + 7) / 8;
-  if (chunks <= 64) return launch3<BF16, OP, 64, 1>(x, g, y, R, C, eps, vec, s);
-  if (chunks <= 128) return launch3<BF16, OP, 64, 2>(x, g, y, R, C, eps, vec, s);
+  if (chunks <= 16) return launch3<BF16, OP, 16, 1>(x, g, y, R, C, eps, vec, s);
+  if (chunks <= 32) return launch3<BF16, OP, 16, 2>(x, g, y, R, C, eps, vec, s);
+  if (chunks <= 64) return launch3<BF16, OP, 16, 4>(x, g, y, R, C, eps, vec, s);
+  if (chunks <= 128) return launch3<BF16, OP, 32, 4>(x, g, y, R, C, eps, vec, s);
   if (chunks <= 256) return launch3<BF16, OP, 64, 4>(x, g, y, R, C, eps, vec, s);
   if (chunks <= 512) return launch3<BF16, OP, 256, 2>(x, g, y, R, C, eps, vec, s);
   if (chunks <= 1024) return launch3<BF16, OP, 256, 4>(x, g, y, R, C, eps, vec, s);
