@@ -867,7 +867,11 @@ extern "C" int64_t fa_fwd_split_count(int64_t B, int64_t H, int64_t Sq, int64_t 
 extern "C" size_t fa_fwd_split_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                                               int64_t n_split) {
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1 || n_split < 0) return 0;
+  const int64_t lim = (int64_t)1 << 31;
+  if (B >= lim || H >= lim || Sq >= lim || Sk >= lim || D > 1024 || B * H >= lim / ((Sq + kBM - 1) / kBM)) return 0;
   const int64_t n = split_plan(B * H, Sq, Sk, n_split).n;
+  // n * B*H*Sq < 2^31 * 128 rows (the grid limit of fa_fwd_split), times (D+1)*4 bytes
+  if (B * H * ((Sq + kBM - 1) / kBM) >= lim / n) return 0;
   return (size_t)n * (size_t)(B * H * Sq) * (size_t)(D + 1) * 4u;
 }
 
@@ -882,6 +886,7 @@ extern "C" fa_status fa_fwd_split(const void* q, const void* k, const void* v, v
   const SplitPlan sp = split_plan(BH, Sq, Sk, n_split);
   const int64_t lim = (int64_t)1 << 31;
   if (BH * ((Sq + kBM - 1) / kBM) >= lim / sp.n) return FA_ERR_INVALID_ARG;
+  if ((BH * Sq + 15) / 16 >= lim) return FA_ERR_INVALID_ARG;  // the merge's grid
   const size_t need = fa_fwd_split_workspace_size(B, H, Sq, Sk, D, n_split);
   if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
   const size_t qo_bytes = (size_t)(BH * Sq * D) * 2, kv_bytes = (size_t)(BH * Sk * D) * 2;
