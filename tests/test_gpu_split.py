@@ -86,6 +86,9 @@ SHAPES = [
     (1, 3, 200, 100, 64, "bf16", True, 7),
     (3, 2, 17, 2049, 64, "bf16", True, 0),
     (1, 1, 129, 777, 128, "f16", True, 4),
+    # D=64 launches of more than 512 work-groups (32-key tiles)
+    (4, 64, 16, 9000, 64, "f16", False, 0),
+    (2, 128, 300, 2000, 64, "bf16", True, 3),
 ]
 
 

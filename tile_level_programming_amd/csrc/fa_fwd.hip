@@ -10,8 +10,9 @@
 // устроен туториал", FlashAttention paragraph).
 //
 // CDNA4 mapping.  One work-group of four waves owns (batch, head, 128
-// queries); each wave owns 32 queries.  Two work-groups share a CU, so every
-// SIMD runs two independent waves; registers stay within 256 per wave.
+// queries); each wave owns 32 queries.  Key tiles are 32 keys long.  At
+// D=64 three work-groups share a CU (registers within 168 per wave), at
+// D=128 two (within 256), so every SIMD runs three or two independent waves.
 //
 //  * Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{f16,bf16}: K (from LDS) is the A operand and the
@@ -232,7 +233,7 @@ template <int I>
 struct Int { static constexpr int value = I; };
 
 template <int D, bool BF16, bool CAUSAL, int BN, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
+__global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kernel(Params p) {
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                     // bytes per row
   constexpr int TILE = BN * ROWB;                 // bytes of one K or V tile
@@ -556,12 +557,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
       for (int db = 0; db < DB; ++db) oacc[db] = mfma_32x32x16<BF16>(v_frag(vt, u, db), pcur[u], oacc[db]);
     const float ts = tile_sum(pnext);
     {
-      // one matrix instruction, then up to three vector instructions and two
-      // LDS reads (the first K fragments are read up front); the vector
+      // one matrix instruction, then up to three (D=64) or two (D=128)
+      // vector instructions and two LDS reads (the first K fragments are read up front); the vector
       // work (per 16-key slice 8 multiplies, 8 exponentials and 4 packs)
       // is spread over most of the step
       constexpr int NMF = NS + NU * DB + NU;
-      constexpr int VPM = 3;
+      constexpr int VPM = D == 64 ? 3 : 2;
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
       for (int i = 0; i < NMF; ++i) {
@@ -696,20 +697,23 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(Params p) {
   }
 }
 
-// Keys per tile for each (head dim, dtype, mask).
-template <int D, bool BF16, bool CAUSAL>
-struct Cfg {
-  static constexpr int BN = D == 64 ? 64 : 32;
-};
+// Keys per tile.  At D=128 always 32 (two work-groups per CU).  At D=64, a
+// launch that fills the chip takes 32-key tiles with three work-groups per CU
+// (measured about 2% faster than 64-key tiles with two); a launch of at most
+// kSmallGrid work-groups, which runs as a single wave of work-groups, takes
+// 64-key tiles: half the steps per work-group, and its latency is the
+// launch's (measured 6% faster on 128 work-groups).
+constexpr int64_t kSmallGrid = 512;
 
 template <int D, bool BF16, bool CAUSAL, bool SPLIT>
 hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream) {
-  using C = Cfg<D, BF16, CAUSAL>;
   Params p = base;
   p.n_qblk = (int)((Sq + kBM - 1) / kBM);
   p.n_wg = (int)(BH * p.n_qblk * p.n_split);
   void* args[] = {&p};
-  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, C::BN, SPLIT>);
+  const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, 32, SPLIT>);
+  if constexpr (D == 64)
+    if (p.n_wg <= kSmallGrid) fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, 64, SPLIT>);
   return hipLaunchKernel(fn, dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
 }
 
