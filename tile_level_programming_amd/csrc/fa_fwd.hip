@@ -104,6 +104,7 @@ struct Params {
   int Sq, Sk;
   int n_qblk;      // query blocks per (b, h)
   int n_wg;        // total work-groups
+  int xcd_heads;   // causal, no split: heads per XCD when every XCD gets whole heads, else 0
   float c;         // |scale| * log2(e)
   uint32_t qsign;  // 0x80008000 when scale < 0 (q is negated on load), else 0
   // split over the keys: range r holds keys r*kchunk .. min(Sk, (r+1)*kchunk)-1
@@ -274,12 +275,25 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
 
   // logical block t = (bh * n_split + range) * n_qblk + query block: the
   // query blocks that read the same keys are neighbours
-  const int t = xcd_remap(blockIdx.x, p.n_wg);
-  const int t2 = t / p.n_qblk;
-  int qblk = t - t2 * p.n_qblk;
-  const int split = SPLIT ? t2 % p.n_split : 0;
-  const int bh = SPLIT ? t2 / p.n_split : t2;
-  if (CAUSAL) qblk = p.n_qblk - 1 - qblk;  // longest blocks first
+  int qblk, split, bh;
+  if (CAUSAL && !SPLIT && p.xcd_heads > 0) {
+    // Every XCD owns xcd_heads whole heads (their keys stay in its L2) and
+    // runs its blocks longest first across all of them: its work-groups
+    // then finish together.  Head by head, longest first within each head,
+    // the long blocks of its last heads would start late.
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int rank = local / p.xcd_heads;  // 0: the longest blocks
+    bh = xcd * p.xcd_heads + (local - rank * p.xcd_heads);
+    qblk = p.n_qblk - 1 - rank;
+    split = 0;
+  } else {
+    const int t = xcd_remap(blockIdx.x, p.n_wg);
+    const int t2 = t / p.n_qblk;
+    qblk = t - t2 * p.n_qblk;
+    split = SPLIT ? t2 % p.n_split : 0;
+    bh = SPLIT ? t2 / p.n_split : t2;
+    if (CAUSAL) qblk = p.n_qblk - 1 - qblk;  // longest blocks first
+  }
   const int q0 = qblk * kBM;
   const int qw0 = q0 + wave * 32;  // first query of this wave
   const int qi = qw0 + n;          // query of this lane
@@ -710,10 +724,22 @@ hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream
   Params p = base;
   p.n_qblk = (int)((Sq + kBM - 1) / kBM);
   p.n_wg = (int)(BH * p.n_qblk * p.n_split);
-  void* args[] = {&p};
   const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, 32, SPLIT>);
+  int per_cu = D == 64 ? 3 : 2;  // work-groups resident per CU
   if constexpr (D == 64)
-    if (p.n_wg <= kSmallGrid) fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, 64, SPLIT>);
+    if (p.n_wg <= kSmallGrid) {
+      fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, 64, SPLIT>);
+      per_cu = 2;
+    }
+  // Causal blocks run longest first across an XCD's heads when a head has
+  // fewer query blocks than the XCD (32 CUs) has work-group slots: head by
+  // head, the long blocks of the XCD's last heads would start late
+  // (simulated: 1.21x the balanced time at 32 blocks on 64 slots, measured
+  // +9% on B4 H16 S4096 D128).  With more blocks per head than slots the
+  // head-by-head order is balanced already and keeps fewer heads' keys in
+  // the XCD's L2 (measured 1.3% faster at 128 blocks on 64 slots).
+  p.xcd_heads = (CAUSAL && !SPLIT && BH % 8 == 0 && p.n_qblk < 32 * per_cu) ? (int)(BH / 8) : 0;
+  void* args[] = {&p};
   return hipLaunchKernel(fn, dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
 }
 
