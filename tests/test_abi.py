@@ -212,3 +212,37 @@ def test_rmsnorm_silu_invalid(fa, kw):
     args.update(kw)
     assert fa.rmsnorm_silu(**args) == fa.FA_ERR_INVALID_ARG
 
+
+
+# --- the torch-level helpers check caller-supplied outputs before any call ---
+
+
+def test_output_checks_on_host_tensors(fa):
+    import torch
+
+    dev = torch.device("cuda", 0)
+    good = dict(shape=(2, 3), dtype=torch.float16, device=dev)
+    with pytest.raises(TypeError):
+        fa._check_out(object(), "out", **good)
+    with pytest.raises(TypeError):
+        fa._check_out(torch.empty(2, 3, dtype=torch.float32), "out", **good)
+    with pytest.raises(ValueError):
+        fa._check_out(torch.empty(2, 4, dtype=torch.float16), "out", **good)
+    with pytest.raises(ValueError):  # right shape and type, but host memory
+        fa._check_out(torch.empty(2, 3, dtype=torch.float16), "out", **good)
+
+
+def test_helpers_reject_host_inputs(fa):
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)
+    with pytest.raises(ValueError):
+        fa.fwd_split(q, q, q)
+    with pytest.raises(ValueError):
+        fa.linear_gelu(torch.zeros(4, 8, dtype=torch.float16), torch.zeros(4, 8, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        fa.softmax(torch.zeros(4, 8, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        fa.lse_merge(torch.zeros(2, 3, 64), torch.zeros(2, 3), torch.float16)

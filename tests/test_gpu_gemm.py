@@ -137,7 +137,8 @@ def test_gemm_deterministic(torch_dev, fa):
 @pytest.mark.parametrize("name", list(fi.GEMM_WORKLOADS))
 def test_gemm_workload_parity(torch_dev, fa, go, name):
     # the benchmarked shapes at full size, on sampled rows the oracle
-    # evaluates one by one (all columns of each)
+    # evaluates one by one (all columns of each): two rows at seeded offsets
+    # in every 256-row block, so every 256 x 256 output tile is checked
     torch = torch_dev
     wl = fi.GEMM_WORKLOADS[name]
     print(f"[gemm] workload {name}", flush=True)
@@ -147,7 +148,10 @@ def test_gemm_workload_parity(torch_dev, fa, go, name):
     c = fa.linear_gelu(ad, wd, bd)
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([[0, 127, 128, wl.M - 1], rng.integers(0, wl.M, 28)]))
+    blocks = np.arange(0, wl.M, 256)
+    rows = np.concatenate([[0, 127, 128, wl.M - 1], blocks + rng.integers(0, 256, blocks.size),
+                           blocks + rng.integers(0, 256, blocks.size)])
+    rows = np.unique(rows[rows < wl.M])
     cs = c[torch.from_numpy(rows).cuda()].float().double().cpu().numpy()
     check(cs, go.gemm_rows(a, w, b, wl.dtype, rows=rows, threads=THREADS), wl.dtype, name)
     assert bool(torch.isfinite(c.float()).all())

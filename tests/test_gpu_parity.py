@@ -77,43 +77,28 @@ def full_check(torch, fa, oracle_mod, q, k, v, dtype, scale, causal, what=""):
     return check(to_f64(torch, o), lse.double().cpu().numpy(), o_ref, lse_ref, dtype, what)
 
 
-def sample_rows(w, n_random=384, seed=0):
-    """Rows the oracle evaluates one by one at full size: the first and last
-    rows of several heads, rows either side of every 64- and 128-row block
-    boundary in a few places, and seeded random rows over all heads."""
-    rng = np.random.default_rng(seed)
-    BH, S = w.B * w.H, w.Sq
-    heads = sorted(set([0, BH - 1, BH // 2] + list(rng.integers(0, BH, 3))))
-    local = set([0, 1, 2, 3, 31, 32, 63, 64, 127, 128, 129, 255, 256, S - 1, S - 2, S - 64, S - 129])
-    local |= set(int(x) for x in rng.integers(0, S, 16))
-    rows = [h * S + i for h in heads for i in sorted(local) if 0 <= i < S]
-    rows += list(rng.integers(0, BH * S, n_random))
-    return np.unique(np.array(rows, dtype=np.int64))
-
-
 # --- the five measured shapes (six runs) -------------------------------------
 
 
 @pytest.mark.parametrize("name", list(fi.WORKLOADS))
 def test_workload_parity(torch_dev, fa, oracle_mod, name):
+    # every row of every workload against the threaded oracle (the largest,
+    # B1 H32 S16384 D128 causal, is about 3e12 float64 operations: well under
+    # a minute on 16 host threads)
     torch = torch_dev
     w = fi.WORKLOADS[name]
-    print(f"[parity] {name}", flush=True)
+    print(f"[parity] {name}: all {w.B * w.H * w.Sq} rows", flush=True)
     q, k, v = fi.make_inputs(w)
-    if w.flops() <= 5e9:
-        full_check(torch, fa, oracle_mod, q, k, v, w.dtype, w.scale, w.causal, name)
-        return
     o, lse = run_gpu(torch, fa, q, k, v, w.dtype, w.scale, w.causal)
-    o = o.view(-1, w.D)
-    lse = lse.view(-1)
-    # every output written and finite
-    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), name
-    rows = sample_rows(w)
-    idx = torch.from_numpy(rows).cuda()
-    o_s = to_f64(torch, o[idx])
-    l_s = lse[idx].double().cpu().numpy()
-    o_ref, l_ref = oracle_mod.attention_rows(q, k, v, w.dtype, w.scale, w.causal, rows, threads=THREADS)
-    check(o_s, l_s, o_ref, l_ref, w.dtype, name)
+    o_gpu, l_gpu = to_f64(torch, o), lse.double().cpu().numpy()
+    del o, lse
+    o_ref, l_ref = oracle_mod.attention(q, k, v, w.dtype, w.scale, w.causal, threads=THREADS)
+    err_o, err_l = check(o_gpu, l_gpu, o_ref, l_ref, w.dtype, name)
+    raw = float(np.abs(l_gpu - l_ref).max())
+    rel_raw = float((np.abs(l_gpu - l_ref) / np.abs(l_ref)).max())
+    small = int((np.abs(l_ref) < 1).sum())
+    print(f"[parity] {name}: max|dO| {err_o:.3e} (bar {TOL_O[w.dtype]:.0e}); lse error guarded {err_l:.3e}, "
+          f"unguarded relative {rel_raw:.3e}, absolute {raw:.3e}; rows with |lse_ref| < 1: {small}", flush=True)
 
 
 # --- ragged and odd shapes ---------------------------------------------------
@@ -190,23 +175,27 @@ def _bits_to_f32(bits, dtype):
 
 
 @pytest.mark.parametrize("D,dtype,H", [(64, "f16", 2), (128, "bf16", 2), (64, "bf16", 2), (128, "f16", 2),
-                                       (64, "f16", 192)])
+                                       (64, "f16", 192), (64, "bf16", 192)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_rising_logits(torch_dev, fa, oracle_mod, D, dtype, H, causal):
     # keys scaled up along the sequence: each row's maximum keeps growing,
     # so the kernel's reference has to move many times, in the branch-free
     # steps and in the masked tail, both before and after a tile's products.
     # At D=64, H=2 runs the 64-key tiles and H=192 (576 work-groups) the
-    # 32-key tiles.  The many-head case is fp16 only: with P rounded to bf16
-    # (relative error up to 2^-9) these nearly one-hot rows reach |dO| about
-    # 2e-2 on some of 192 heads, on either tile length alike.
+    # 32-key tiles.  The dominant keys of these nearly one-hot rows sit in
+    # the masked tail, whose P (up to the sum bound above the reference) bf16
+    # rounds by up to 2^-9: the normaliser must sum the same rounded P as the
+    # P.V product there too, or O is scaled by the rounding (bf16, 192 heads:
+    # max |dO| 2.05e-2 with fp32 sums of the unrounded P on those steps).
     Sq, Sk = 300, 2000
     q = fi.tensor_bits(24, "q", (1, H, Sq, D), dtype, 2.0)
     k0 = _bits_to_f32(fi.tensor_bits(24, "k", (1, H, Sk, D), dtype), dtype)
     ramp = (0.25 + 6.0 * np.arange(Sk, dtype=np.float32) / Sk)[None, None, :, None]
     k = fi.f32_to_bits(k0 * ramp, dtype)
     v = fi.tensor_bits(24, "v", (1, H, Sk, D), dtype)
-    full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(D), causal, f"rising {D} {dtype}")
+    err_o, err_l = full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(D), causal,
+                              f"rising {D} {dtype}")
+    print(f"[rising] D={D} {dtype} H={H} causal={causal}: max|dO| {err_o:.4e} lse err {err_l:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("D,dtype,H", [(64, "f16", 2), (128, "bf16", 2), (64, "f16", 180)])
@@ -327,3 +316,27 @@ def test_device_errors_are_host_errors(torch_dev, fa):
         fa.fwd(torch.zeros(1, 1, 8, 96, dtype=torch.float16, device="cuda"),
                torch.zeros(1, 1, 8, 96, dtype=torch.float16, device="cuda"),
                torch.zeros(1, 1, 8, 96, dtype=torch.float16, device="cuda"))
+
+
+def test_bad_outputs_rejected_before_launch(torch_dev, fa):
+    torch = torch_dev
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q, out=torch.empty(1, 2, 7, 64, dtype=torch.float16, device="cuda"))
+    with pytest.raises(TypeError):
+        fa.fwd(q, q, q, out=torch.empty(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q, out=torch.empty(1, 2, 64, 8, dtype=torch.float16, device="cuda").transpose(2, 3))
+    with pytest.raises(TypeError):
+        fa.fwd(q, q, q, lse=torch.empty(1, 2, 8, dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q, lse=torch.empty(1, 2, 8, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        fa.fwd_split(q, q, q, lse=torch.empty(2, 8, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.linear_gelu(torch.zeros(4, 8, dtype=torch.float16, device="cuda"),
+                       torch.zeros(6, 8, dtype=torch.float16, device="cuda"),
+                       out=torch.empty(4, 5, dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.softmax(torch.zeros(4, 8, dtype=torch.float16, device="cuda"),
+                   out=torch.empty(4, 8, dtype=torch.float16))

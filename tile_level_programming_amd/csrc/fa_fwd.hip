@@ -151,6 +151,20 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   }
 }
 
+// The two 16-bit values of a packed pair, back in fp32 (exact), added: the
+// normaliser that divides O is the sum of the same rounded P that the P.V
+// product multiplies, so O is a convex combination of the V rows with the
+// rounded weights.
+template <bool BF16>
+__device__ __forceinline__ float sum_pair(uint32_t x) {
+  if constexpr (BF16) {
+    return __builtin_bit_cast(float, x << 16) + __builtin_bit_cast(float, x & 0xffff0000u);
+  } else {
+    const f16x2 h = __builtin_bit_cast(f16x2, x);
+    return (float)h[0] + (float)h[1];
+  }
+}
+
 // v_permlane32_swap exchanges the two 32-lane halves of a wave: afterwards
 // the pair holds, in every lane, the values of lane l%32 and lane l%32+32.
 __device__ __forceinline__ float max_halves(float x) {
@@ -390,7 +404,16 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
   // 16 accumulator slots instead of from 0, so the subtraction costs no
   // instruction.
   float m_ref = 0.f;
-  float l_run = 0.f;        // running normaliser of this lane's query (both halves hold it)
+  // Running normaliser of this lane's query (both halves hold it): the sum
+  // of the rounded P, which divides O.  lse takes l_run + l_corr, where
+  // l_corr collects the rounding (unrounded minus rounded P) of the tiles
+  // that the vector unit sums: the first tile, the masked tiles and the
+  // re-referenced ones.  A short causal row lies wholly in such tiles, so
+  // its lse is that of the unrounded P (bf16 rounds P by up to 2^-9, which
+  // would otherwise reach ~1e-3 in the lse of a row of a few keys); over the
+  // branch-free tiles the rounding errors of many keys average out.
+  float l_run = 0.f;
+  float l_corr = 0.f;
   const float c = p.c;      // raw score -> exp2 units
   f32x16 negm;
   auto set_negm = [&]() __attribute__((always_inline)) {
@@ -444,13 +467,17 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
   };
 
-  // P = exp2(s*c) of the relative scores, packed to 16 bits
-  // into pout; returns this lane's sum of the tile's P in fp32 (half of the
-  // tile's keys: sum_halves gives the row's).  The branch-free steps ignore
-  // it and take the row sums on the matrix unit (tile_sum).
-  auto tile_exp = [&](const f32x16* sacc, u32x4* pout, auto mask_tag) __attribute__((always_inline)) -> float {
+  // P = exp2(s*c) of the relative scores, packed to 16 bits into pout;
+  // returns this lane's sums, in fp32, of the tile's P as rounded to 16 bits
+  // (r) and of the rounding, unrounded minus rounded (d), over half of the
+  // tile's keys (sum_halves gives the row's).  The branch-free steps ignore
+  // them and take the rounded sums on the matrix unit (tile_sum).
+  struct Sums {
+    float r, d;
+  };
+  auto tile_exp = [&](const f32x16* sacc, u32x4* pout, auto mask_tag) __attribute__((always_inline)) -> Sums {
     constexpr bool MASK = decltype(mask_tag)::value;
-    float ps[2];
+    float ps[2], pu[2];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       float pv[8];
@@ -464,11 +491,14 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pout[u][e] = pack2<BF16>(pv[2 * e], pv[2 * e + 1]);
-        const float pair = pv[2 * e] + pv[2 * e + 1];
+        const float pair = sum_pair<BF16>(pout[u][e]);
+        const float upair = pv[2 * e] + pv[2 * e + 1];
         ps[e & 1] = (u == 0 && e < 2) ? pair : ps[e & 1] + pair;
+        pu[e & 1] = (u == 0 && e < 2) ? upair : pu[e & 1] + upair;
       }
     }
-    return ps[0] + ps[1];
+    const float r = ps[0] + ps[1];
+    return Sums{r, (pu[0] + pu[1]) - r};
   };
 
   // Row sums of a tile's packed P on the matrix unit: four 16x16x32
@@ -516,7 +546,9 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
       }
     const float alpha = exp2f(-delta * c);
     scale_o(alpha);
-    l_run = l_run * alpha + sum_halves(tile_exp(st, pout, Flag<true>{}));
+    const Sums ts = tile_exp(st, pout, Flag<true>{});
+    l_run = l_run * alpha + sum_halves(ts.r);
+    l_corr = l_corr * alpha + sum_halves(ts.d);
   };
   // set by a step whose exponentials hit the bound: the next step, before
   // its products, re-references that tile (its scores are still in the
@@ -609,17 +641,22 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
       const char* vt = vbuf(j & 3);
       if (redo) reref(snext, pcur, scur);
       if (j + 2 < nt_w) score_tile(snext, kt);
-      float ts = 0.f;
+      float ts = 0.f, td = 0.f;
       if (j + 1 < nt_w) {
         apply_mask(scur, (j + 1) * BN);
-        ts = sum_halves(tile_exp(scur, pnext, Flag<true>{}));
+        const Sums t2 = tile_exp(scur, pnext, Flag<true>{});
+        ts = sum_halves(t2.r);
+        td = sum_halves(t2.d);
       }
 #pragma unroll
       for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] = mfma_32x32x16<BF16>(v_frag(vt, u, db), pcur[u], oacc[db]);
       redo = __builtin_amdgcn_ballot_w64(ts > kSumBound) != 0;
-      if (!redo) l_run += ts;
+      if (!redo) {
+        l_run += ts;
+        l_corr += td;
+      }
     }
   };
 
@@ -643,7 +680,9 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sa[kb][r] -= m_ref;
-    l_run = sum_halves(tile_exp(sa, pa, Flag<true>{}));
+    const Sums t0 = tile_exp(sa, pa, Flag<true>{});
+    l_run = sum_halves(t0.r);
+    l_corr = sum_halves(t0.d);
     score_tile(sb, kbuf(1));
   }
 
@@ -689,7 +728,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
         for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * gq + e] * inv;
         *reinterpret_cast<f32x4*>(op + d0) = w;
       }
-    if (h == 0) p.plse[row] = l == 0.f ? -INFINITY : (m_ref * c + __log2f(l)) * kLn2;
+    if (h == 0) p.plse[row] = l == 0.f ? -INFINITY : (m_ref * c + __log2f(l + l_corr)) * kLn2;
   }
   if (!SPLIT && qw0 < p.Sq) {
     const float l = l_run;
@@ -706,7 +745,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
           w[1] = pack2<BF16>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
           *reinterpret_cast<u32x2*>(og + d0) = w;
         }
-      if (h == 0) p.lse[(size_t)bh * p.Sq + qi] = (m_ref * c + __log2f(l)) * kLn2;
+      if (h == 0) p.lse[(size_t)bh * p.Sq + qi] = (m_ref * c + __log2f(l + l_corr)) * kLn2;
     }
   }
 }

@@ -131,20 +131,22 @@ __global__ __launch_bounds__(kThreads) void rowwise_kernel(const uint16_t* __res
       for (int e = 0; e < 8; ++e)
         if (valid(i, e)) m = __builtin_elementwise_maximum(m, elem<BF16>(v[i], e));
     m = group_reduce<TPR, true>(m, red);
-    const float mc = m * kLog2e;
+    // exp(x - m) as exp2((x - m) log2 e), the difference taken first: m
+    // log2 e would overflow for a bf16 row whose maximum is above about
+    // 2.4e38 and turn the whole row into NaN
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (valid(i, e)) s += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<BF16>(v[i], e), kLog2e, -mc));
+        if (valid(i, e)) s += __builtin_amdgcn_exp2f((elem<BF16>(v[i], e) - m) * kLog2e);
     s = group_reduce<TPR, false>(s, red);
     const float inv = 1.f / s;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(elem<BF16>(v[i], e), kLog2e, -mc)) * inv;
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f((elem<BF16>(v[i], e) - m) * kLog2e) * inv;
       u32x4 o;
 #pragma unroll
       for (int k = 0; k < 4; ++k) o[k] = pack2<BF16>(p[2 * k], p[2 * k + 1]);

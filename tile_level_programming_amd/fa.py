@@ -121,8 +121,10 @@ def linear_gelu(a, w, bias=None, out=None):
     for t in (a, w) + ((bias,) if bias is not None else ()):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("a, w, bias must be contiguous device tensors")
+    _check_same_device(a.device, w, *((bias,) if bias is not None else ()))
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check_out(out, "out", (M, N), a.dtype, a.device)
     dt = FA_F16 if a.dtype == torch.float16 else FA_BF16
     stream = torch.cuda.current_stream(a.device).cuda_stream
     st = gemm_bias_gelu(a.data_ptr(), w.data_ptr(), 0 if bias is None else bias.data_ptr(), out.data_ptr(),
@@ -149,8 +151,13 @@ def _rows_call(x, extra, fn, out):
         raise TypeError("x must be a [R, C] float16 or bfloat16 tensor")
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous device tensor")
+    if extra is not None:
+        if not extra.is_cuda:
+            raise ValueError("g must be a device tensor")
+        _check_same_device(x.device, extra)
     if out is None:
         out = torch.empty_like(x)
+    _check_out(out, "out", x.shape, x.dtype, x.device)
     dt = FA_F16 if x.dtype == torch.float16 else FA_BF16
     st = fn(x, out, dt, torch.cuda.current_stream(x.device).cuda_stream)
     if st != FA_OK:
@@ -166,7 +173,7 @@ def softmax(x, out=None):
 
 def rmsnorm_silu_rows(x, g, eps: float = 1e-6, out=None):
     """silu(x / rms(x) * g) along the rows of a [R, C] device tensor; g [C]."""
-    if g.dtype != x.dtype or tuple(g.shape) != (x.shape[1],) or not g.is_contiguous():
+    if x.dim() != 2 or g.dtype != x.dtype or tuple(g.shape) != (x.shape[1],) or not g.is_contiguous():
         raise ValueError("g must be a contiguous [C] tensor of x's dtype")
     return _rows_call(x, g, lambda t, o, dt, s: rmsnorm_silu(t.data_ptr(), g.data_ptr(), o.data_ptr(), t.shape[0],
                                                              t.shape[1], eps, dt, s), out)
@@ -196,11 +203,36 @@ def _check(q, k, v):
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
+    _check_same_device(q.device, k, v)
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
     if tuple(k.shape) != (B, H, Sk, D) or tuple(v.shape) != (B, H, Sk, D):
         raise ValueError("k and v must be [B, H, Sk, D] matching q")
     return B, H, Sq, Sk, D
+
+
+def _check_out(t, name, shape, dtype, device):
+    """A caller-supplied output must match what the kernel writes exactly:
+    the C ABI only sees a pointer, so a smaller, mistyped, strided or host
+    tensor would be written past its end or fault the device."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_same_device(device, *ts):
+    for t in ts:
+        if t.device != device:
+            raise ValueError(f"all tensors must be on {device}; got one on {t.device}")
 
 
 def fwd_split(q, k, v, causal: bool = False, scale: float | None = None, n_split: int = 0, out=None,
@@ -221,9 +253,12 @@ def fwd_split(q, k, v, causal: bool = False, scale: float | None = None, n_split
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _check_out(out, "out", q.shape, q.dtype, q.device)
+    _check_out(lse, "lse", (B, H, Sq), torch.float32, q.device)
     need = split_workspace_size(B, H, Sq, Sk, D, n_split)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_out(workspace, "workspace", (workspace.numel(),), workspace.dtype, q.device)
     dt = FA_F16 if q.dtype == torch.float16 else FA_BF16
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -243,6 +278,11 @@ def lse_merge(o_parts, lse_parts, dtype):
     lead = tuple(lse_parts.shape[1:])
     if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
         raise TypeError("partials must be float32")
+    if dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("dtype must be torch.float16 or torch.bfloat16")
+    if not o_parts.is_cuda or not lse_parts.is_cuda:
+        raise ValueError("partials must be device tensors")
+    _check_same_device(o_parts.device, lse_parts)
     if tuple(o_parts.shape) != (G, *lead, D) or lse_parts.shape[0] != G:
         raise ValueError("o_parts must be [G, ..., D] and lse_parts [G, ...]")
     if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
@@ -271,25 +311,15 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
 
     import torch
 
-    if q.dtype not in (torch.float16, torch.bfloat16):
-        raise TypeError("q, k, v must be float16 or bfloat16")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, S, D]")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
-    B, H, Sq, D = q.shape
-    Sk = k.shape[2]
-    if tuple(k.shape) != (B, H, Sk, D) or tuple(v.shape) != (B, H, Sk, D):
-        raise ValueError("k and v must be [B, H, Sk, D] matching q")
+    B, H, Sq, Sk, D = _check(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _check_out(out, "out", q.shape, q.dtype, q.device)
+    _check_out(lse, "lse", (B, H, Sq), torch.float32, q.device)
     dt = FA_F16 if q.dtype == torch.float16 else FA_BF16
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
