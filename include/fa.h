@@ -39,7 +39,8 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, bad size, overlap, non-finite scale */
     FA_ERR_UNSUPPORTED = 2,  /* head dimension or dtype this build does not provide */
-    FA_ERR_LAUNCH = 3        /* the HIP runtime refused the kernel launch */
+    FA_ERR_LAUNCH = 3,       /* the HIP runtime refused the kernel launch (or a HIP query failed) */
+    FA_ERR_SCRATCH_TOO_SMALL = 4  /* fa_fwd_split_noalloc: partials larger than FA_SPLIT_SCRATCH_BYTES */
 } fa_status;
 
 /*
@@ -133,6 +134,36 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                        float scale, int causal, int dtype, int64_t n_split,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Size of the fixed device buffer of fa_fwd_split_noalloc: 32 MiB, held by
+ * every device the library runs on from the first such call until the
+ * process ends.
+ */
+#define FA_SPLIT_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+/*
+ * fa_fwd_split_noalloc -- fa_fwd_split with its partial results in a fixed
+ * device buffer inside the library instead of a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  It calls no
+ * allocating routine.
+ *
+ * Arguments, checks, results and asynchrony as for fa_fwd_split, without
+ * the workspace.  The partials must fit the buffer:
+ * fa_fwd_split_workspace_size(B, H, Sq, Sk, D, n_split) <= FA_SPLIT_SCRATCH_BYTES,
+ * else FA_ERR_SCRATCH_TOO_SMALL and nothing is launched (a smaller n_split
+ * needs less).  The buffer's device address is looked up on the first call
+ * made with a device current (hipGetDevice), so `stream` must belong to the
+ * current device.  Every call on a device shares that device's buffer, which
+ * keeps the last call's partials: calls that overlap on one device (other
+ * streams, or other threads, without ordering between them) race and give
+ * wrong results.  Nothing in the buffer needs to start at zero: each call
+ * writes every partial it reads.
+ */
+fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                               float scale, int causal, int dtype, int64_t n_split, void* stream);
 
 /*
  * fa_lse_merge -- enqueue the log-sum-exp merge of partial attention results

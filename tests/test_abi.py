@@ -29,9 +29,9 @@ def fa():
 
 
 def test_header_declares_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_fwd_split", "fa_fwd_split_count", "fa_fwd_split_workspace_size",
-                                     "fa_lse_merge", "fa_status_string", "gemm_bias_gelu", "rmsnorm_silu",
-                                     "row_softmax"]
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_split", "fa_fwd_split_count", "fa_fwd_split_noalloc",
+                                     "fa_fwd_split_workspace_size", "fa_lse_merge", "fa_status_string",
+                                     "gemm_bias_gelu", "rmsnorm_silu", "row_softmax"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -138,6 +138,35 @@ def test_split_invalid_arguments(fa, kw):
 @pytest.mark.parametrize("kw", [dict(D=96), dict(dtype=2)])
 def test_split_unsupported(fa, kw):
     assert _call_split(fa, **kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def _call_noalloc(fa, **kw):
+    args = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, Sq=16, Sk=1024, D=64,
+                scale=0.125, causal=0, dtype=fa.FA_F16, n_split=4, stream=0)
+    args.update(kw)
+    return fa.fa_fwd_split_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(lse=0), dict(o=A + 8), dict(Sk=0), dict(B=0), dict(scale=float("inf")),
+    dict(n_split=-1), dict(o=A), dict(lse=3 * A + 64),  # outputs overlapping inputs
+])
+def test_noalloc_invalid_arguments(fa, kw):
+    assert _call_noalloc(fa, **kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(D=96), dict(dtype=2)])
+def test_noalloc_unsupported(fa, kw):
+    assert _call_noalloc(fa, **kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_partials_beyond_the_scratch(fa):
+    # these checks return before any HIP call, so they run without a GPU
+    B, H, Sq, Sk, D = 1, 1, 100000, 1024, 128
+    assert fa.split_workspace_size(B, H, Sq, Sk, D, 4) > fa.SPLIT_SCRATCH_BYTES
+    st = _call_noalloc(fa, o=64 * A, lse=128 * A, B=B, H=H, Sq=Sq, Sk=Sk, D=D, n_split=4)
+    assert st == fa.FA_ERR_SCRATCH_TOO_SMALL
+    assert "scratch" in fa.fa_status_string(st)
 
 
 def _call_merge(fa, **kw):

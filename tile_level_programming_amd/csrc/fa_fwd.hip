@@ -66,7 +66,17 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "fa.h"
+
+// Fixed device buffer of fa_fwd_split_noalloc: the partial results of the
+// key split live here instead of in a caller workspace.  Each device the
+// library runs on holds its own copy until the process ends.  In host code
+// this name is only a handle for hipGetSymbolAddress; the device address is
+// looked up once per device (scratch_on_current_device) and passed to the
+// kernels like any workspace.
+static __device__ __align__(256) unsigned char scratch[FA_SPLIT_SCRATCH_BYTES];
 
 namespace {
 
@@ -944,10 +954,13 @@ extern "C" size_t fa_fwd_split_workspace_size(int64_t B, int64_t H, int64_t Sq, 
   return (size_t)n * (size_t)(B * H * Sq) * (size_t)(D + 1) * 4u;
 }
 
-extern "C" fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
-                                  int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                                  float scale, int causal, int dtype, int64_t n_split,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// The key split with its partials in `workspace` (a caller buffer or the
+// fixed scratch): argument checks, the partial-result kernel, the merge.
+fa_status split_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t Sq, int64_t Sk, int64_t D, float scale, int causal, int dtype, int64_t n_split,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   fa_status st = check_attention_args(q, k, v, o, lse, B, H, Sq, Sk, D, scale, dtype);
   if (st != FA_OK) return st;
   if (n_split < 0 || !workspace || ((uintptr_t)workspace & 15u)) return FA_ERR_INVALID_ARG;
@@ -975,6 +988,55 @@ extern "C" fa_status fa_fwd_split(const void* q, const void* k, const void* v, v
   if (launch_any<true>(p, BH, Sq, D, bf, causal != 0, s) != hipSuccess) return FA_ERR_LAUNCH;
   if (launch_merge(p.po, p.plse, sp.n, BH * Sq, D, bf, o, lse, s) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept: every device has its own copy
+// of the array at its own address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fa_status scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_LAUNCH;
+  if (dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                  float scale, int causal, int dtype, int64_t n_split,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return split_impl(q, k, v, o, lse, B, H, Sq, Sk, D, scale, causal, dtype, n_split, workspace,
+                    workspace_bytes, stream);
+}
+
+extern "C" fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                          int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                          float scale, int causal, int dtype, int64_t n_split, void* stream) {
+  // the same checks as fa_fwd_split first, so that a bad argument is
+  // reported as such and not as a size beyond the scratch
+  fa_status st = check_attention_args(q, k, v, o, lse, B, H, Sq, Sk, D, scale, dtype);
+  if (st != FA_OK) return st;
+  if (n_split < 0) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_fwd_split_workspace_size(B, H, Sq, Sk, D, n_split);
+  if (need == 0) return FA_ERR_INVALID_ARG;
+  if (need > (size_t)FA_SPLIT_SCRATCH_BYTES) return FA_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != FA_OK) return st;
+  return split_impl(q, k, v, o, lse, B, H, Sq, Sk, D, scale, causal, dtype, n_split, ws,
+                    (size_t)FA_SPLIT_SCRATCH_BYTES, stream);
 }
 
 extern "C" fa_status fa_lse_merge(const float* o_parts, const float* lse_parts, int64_t n_part, int64_t rows,
@@ -1006,6 +1068,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCRATCH_TOO_SMALL: return "partial results exceed the library's fixed scratch buffer";
     default: return "unknown status";
   }
 }

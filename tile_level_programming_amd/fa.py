@@ -23,6 +23,8 @@ FA_OK = 0
 FA_ERR_INVALID_ARG = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_LAUNCH = 3
+FA_ERR_SCRATCH_TOO_SMALL = 4
+SPLIT_SCRATCH_BYTES = 32 * 1024 * 1024  # FA_SPLIT_SCRATCH_BYTES of include/fa.h
 
 
 class FaError(RuntimeError):
@@ -53,6 +55,12 @@ def _load():
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.fa_fwd_split_noalloc.restype = ctypes.c_int
+    lib.fa_fwd_split_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int64, ctypes.c_void_p]
     lib.fa_lse_merge.restype = ctypes.c_int
     lib.fa_lse_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -90,6 +98,14 @@ def fa_fwd_split(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: i
     """Direct call of the C entry point with raw device addresses; returns the status."""
     return int(_lib.fa_fwd_split(q, k, v, o, lse, B, H, Sq, Sk, D, scale, int(causal), int(dtype),
                                  int(n_split), workspace, int(workspace_bytes), stream))
+
+
+def fa_fwd_split_noalloc(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int, Sk: int, D: int,
+                         scale: float, causal: int, dtype: int, n_split: int, stream: int) -> int:
+    """Direct call of the C entry point (partials in the library's fixed device
+    buffer, no allocation) with raw device addresses; returns the status."""
+    return int(_lib.fa_fwd_split_noalloc(q, k, v, o, lse, B, H, Sq, Sk, D, scale, int(causal), int(dtype),
+                                         int(n_split), stream))
 
 
 def fa_lse_merge(o_parts: int, lse_parts: int, n_part: int, rows: int, D: int, o: int, lse: int, dtype: int,
