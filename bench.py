@@ -131,8 +131,12 @@ def host_fields(threads: int) -> dict:
 
 class ClockSampler:
     """Samples the graphics clock with AMD SMI (GPU metrics) on a side thread
-    while the timed region runs.  Reports None when the metrics are not
-    readable (the figure is then absent, never guessed)."""
+    while the timed region runs.  The metrics table refreshes a few times a
+    second, so a reading counts only once it shows the GPU busy (graphics
+    activity >= 50%): the first readings of a region still describe the idle
+    GPU before it.  The clock is the mean over the 8 XCDs' graphics clocks.
+    Reports None when the metrics are not readable or never showed the load
+    (the figure is then absent, never guessed)."""
 
     def __init__(self, period_s: float = 0.002):
         self.period = period_s
@@ -170,6 +174,9 @@ class ClockSampler:
 
     def _read(self):
         m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+        act = m.get("average_gfx_activity")
+        if not isinstance(act, (int, float)) or act < 50:
+            return None
         clks = m.get("current_gfxclks")
         if isinstance(clks, (list, tuple)):
             vals = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 10000]
@@ -219,11 +226,11 @@ class ClockSampler:
             return {"mean_mhz": None, "samples": 0, "source": "AMD SMI GPU metrics",
                     "error": self.error or "no readable samples"}
         s = np.array(self.samples)
-        # the region's first samples can precede the first launch reaching the GPU
         return {"mean_mhz": round(float(s.mean()), 1), "median_mhz": round(float(np.median(s)), 1),
                 "min_mhz": round(float(s.min()), 1), "max_mhz": round(float(s.max()), 1),
-                "samples": int(s.size), "source": "AMD SMI GPU metrics (graphics clock), sampled every "
-                f"{self.period * 1e3:.0f} ms during the timed region"}
+                "samples": int(s.size), "source": "AMD SMI GPU metrics: mean graphics clock of the 8 XCDs, "
+                f"sampled every {self.period * 1e3:.0f} ms during the timed region, readings with graphics "
+                "activity >= 50%"}
 
 
 def peak_at_clock(peak: float, clock: dict):
@@ -234,14 +241,23 @@ def peak_at_clock(peak: float, clock: dict):
 # --- timing -------------------------------------------------------------------
 
 
-def time_steps(step, stream, steps: int, warmup: int):
+def time_steps(step, stream, steps, warmup: int):
     """W untimed warmup steps, then K timed steps on ``stream``: one event pair
-    around the whole region and one around every launch."""
+    around the whole region and one around every launch.  K = None picks a
+    count that makes the region about 2 s long (at least 200 steps, at most
+    20000): the clock readings need a region of a second or more."""
     import torch
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    if steps is None:
+        t0 = time.perf_counter()
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / 10
+        steps = int(min(20000, max(200, 2.0 / max(per, 1e-7))))
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -258,7 +274,7 @@ def time_steps(step, stream, steps: int, warmup: int):
         wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / steps
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    return ms, launch_ms, wall, clk.result()
+    return ms, launch_ms, wall, clk.result(), steps
 
 
 # --- the oracle on the host ------------------------------------------------------
@@ -364,14 +380,14 @@ def run_attention(args, w):
         if st != fa.FA_OK:
             raise fa.FaError(st)
 
-    log(f"[bench] warmup {args.warmup}, then {args.steps} timed steps")
-    ms, launch_ms, wall, clock = time_steps(step, stream, args.steps, args.warmup)
+    log(f"[bench] warmup {args.warmup}, then {args.steps or 'about 2 s of'} timed steps")
+    ms, launch_ms, wall, clock, steps = time_steps(step, stream, args.steps, args.warmup)
     ms_kernel = float(np.mean(launch_ms))
     flop = w.flops()
     tflops = flop / (ms * 1e-3) / 1e12
     tflops_kernel = flop / (ms_kernel * 1e-3) / 1e12
     gbs_kernel = w.io_bytes() / (ms_kernel * 1e-3) / 1e9
-    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s; per launch "
+    log(f"[bench] {steps} steps: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s; per launch "
         f"mean {ms_kernel:.4f} ms (min {min(launch_ms):.4f}, max {max(launch_ms):.4f}), "
         f"{tflops_kernel:.1f} TFLOP/s, {gbs_kernel:.0f} GB/s of algorithmic bytes (wall {wall:.3f} s); "
         f"clock {clock.get('median_mhz')} MHz")
@@ -381,7 +397,7 @@ def run_attention(args, w):
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
@@ -483,12 +499,12 @@ def run_gemm(args, w):
         if st != fa.FA_OK:
             raise fa.FaError(st)
 
-    ms, launch_ms, wall, clock = time_steps(step, stream, args.steps, args.warmup)
+    ms, launch_ms, wall, clock, steps = time_steps(step, stream, args.steps, args.warmup)
     ms_kernel = float(np.mean(launch_ms))
     flop = w.flops()
     tflops = flop / (ms * 1e-3) / 1e12
     tflops_kernel = flop / (ms_kernel * 1e-3) / 1e12
-    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s; per launch mean {ms_kernel:.4f} ms "
+    log(f"[bench] {steps} steps: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s; per launch mean {ms_kernel:.4f} ms "
         f"(min {min(launch_ms):.4f}, max {max(launch_ms):.4f}), {tflops_kernel:.1f} TFLOP/s")
 
     if args.no_check:
@@ -535,7 +551,7 @@ def run_gemm(args, w):
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
@@ -588,12 +604,12 @@ def run_rows(args, w):
         if st != fa.FA_OK:
             raise fa.FaError(st)
 
-    ms, launch_ms, wall, clock = time_steps(step, stream, args.steps, args.warmup)
+    ms, launch_ms, wall, clock, steps = time_steps(step, stream, args.steps, args.warmup)
     ms_kernel = float(np.mean(launch_ms))
     nbytes = w.io_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     gbs_kernel = nbytes / (ms_kernel * 1e-3) / 1e9
-    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step, {gbs:.0f} GB/s; per launch mean {ms_kernel:.4f} ms "
+    log(f"[bench] {steps} steps: {ms:.4f} ms/step, {gbs:.0f} GB/s; per launch mean {ms_kernel:.4f} ms "
         f"(min {min(launch_ms):.4f}, max {max(launch_ms):.4f}), {gbs_kernel:.0f} GB/s")
 
     if args.no_check:
@@ -621,7 +637,7 @@ def run_rows(args, w):
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
@@ -652,7 +668,8 @@ def run_one(args, name):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: enough for about 2 s, at least 200)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=fi.HEADLINE, choices=list(fi.ALL_WORKLOADS) + list(fi.GEMM_WORKLOADS)
                     + list(fi.ROW_WORKLOADS))
