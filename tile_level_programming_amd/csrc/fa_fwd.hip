@@ -235,20 +235,23 @@ __device__ __forceinline__ int vsw(int r) {
 
 // Stream NLD 1 KB blocks of one tensor's rows k0.. into LDS.  Lane l of
 // block i fills bytes 16l..16l+15 of the block at dst + i*stride, reading the
-// bytes at off[i] of the rows from key k0 on; the buffer range ends at key
-// Sk, so rows past it arrive as zeros.  A tile wholly past the keys gets an
-// empty range: its loads touch no memory, write zeros and still count in
-// vmcnt, which keeps the number of loads in flight the same every step.
+// bytes at off[i] of the rows from key k0 on.  `r` is one buffer resource
+// for the whole key range, made once: the tile's start goes into each lane's
+// offset, so the range check (offset below the range's size) zero-fills the
+// rows past the last key and a tile wholly past the keys touches no memory.
+// Its loads still count in vmcnt, which keeps the number of loads in flight
+// the same every step.  The offsets are 32-bit: K and V are below 2^32 bytes
+// per head (Sk*D < 2^31), and an offset of a tile past the end that wraps
+// lands inside the range, where it reads real rows into a stage no product
+// uses.
 template <int NLD>
-__device__ __forceinline__ void load_rows_to_lds(const uint16_t* g, int k0, int Sk, int rowb, char* dst,
-                                                 int stride, const int* off) {
-  const bool any = k0 < Sk;
-  const uint32_t bytes = any ? (uint32_t)(Sk - k0) * (uint32_t)rowb : 0u;
-  const char* base = (const char*)g + (any ? (size_t)k0 * rowb : 0);
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufferWord3);
+__device__ __forceinline__ void load_rows_to_lds(__amdgpu_buffer_rsrc_t r, int k0, int rowb, char* dst, int stride,
+                                                 const int* off) {
+  const uint32_t base = (uint32_t)k0 * (uint32_t)rowb;
 #pragma unroll
   for (int i = 0; i < NLD; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * stride), 16, off[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * stride), 16, (int)(base + (uint32_t)off[i]),
+                                             0, 0, 0);
 }
 
 template <bool B>
@@ -358,22 +361,31 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     offk[i] = r * ROWB + ((pc ^ ksw<D>(r)) << 4);
     offv[i] = r * ROWB + ((pc ^ vsw<D>(r)) << 4);
   }
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, (uint32_t)Skl * ROWB, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (uint32_t)Skl * ROWB, kBufferWord3);
   auto issue_k = [&](int tile, char* buf) __attribute__((always_inline)) {
-    load_rows_to_lds<NLD>(kg, tile * BN, Skl, ROWB, buf + wave * 1024, kWaves * 1024, offk);
+    load_rows_to_lds<NLD>(rk, tile * BN, ROWB, buf + wave * 1024, kWaves * 1024, offk);
   };
   auto issue_v = [&](int tile, char* buf) __attribute__((always_inline)) {
-    load_rows_to_lds<NLD>(vg, tile * BN, Skl, ROWB, buf + wave * 1024, kWaves * 1024, offv);
+    load_rows_to_lds<NLD>(rv, tile * BN, ROWB, buf + wave * 1024, kWaves * 1024, offv);
   };
 
-  // K 0 and K 1 first (the prologue's scores), then K 2 and V 0 (step 0),
-  // K 3 and V 1 (step 1); every step then issues 2*NLD loads (K j+4, V j+2),
-  // past the keys included, so each wait has a fixed count
+  // Tile t of K lands two steps before its fragments are read (at the end of
+  // step t-3), tile t of V three steps before it is read (step t): step j
+  // issues K j+5 and V j+3, and waits for the loads of step j-2.  K 0 and
+  // K 1 come first (the prologue's scores), then K 2 (the first fragments
+  // read ahead), V 0, K 3, V 1, V 2; K 4 goes into K 0's stage once every
+  // wave has read K 0.  Every step issues 2*NLD loads, past the keys
+  // included, so each wait has a fixed count.
   issue_k(0, kbuf(0));
   issue_k(1, kbuf(1));
   issue_k(2, kbuf(2));
   issue_v(0, vbuf(0));
   issue_k(3, kbuf(3));
   issue_v(1, vbuf(1));
+  issue_v(2, vbuf(2));
 
   // ---- Q fragments: B operands of S^T = K Q^T; lane holds q[qi][16*ks + 8*h .. +8]
   u32x4 qf[DK];
@@ -582,21 +594,23 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     constexpr int jm = decltype(jm4_tag)::value;  // j % 4
     // The wait and the barrier in one asm statement with a memory clobber:
     // no LDS access moves across it, and no release fence makes the compiler
-    // wait for the loads still in flight (they target other stages).  Only
-    // the V loads of the previous step may stay in flight: its K loads (tile
-    // j+3) are read at the end of this step, for the next one.  LDS reads
-    // need not have returned: the stages this step overwrites (K tile j, V
-    // tile j-2) were last read, and their fragments used, two steps ago.
+    // wait for the loads still in flight (they target other stages).  The
+    // loads of the previous step may stay in flight; those of step j-2 (K
+    // tile j+3, read at the end of this step for the next one, and V tile
+    // j+1) have landed.  LDS reads need not have returned: the stages this
+    // step overwrites (K tile j+1, whose fragments were read at the end of
+    // step j-2, and V tile j-1, read in step j-1) were consumed by the
+    // products of the previous step, before this barrier.
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NLD) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NLD) : "memory");
     __builtin_amdgcn_sched_barrier(0);
     // the step's products and exponentials run at raised issue priority;
     // the row-sum check and the wait at the next barrier run at the normal
     // one, so a SIMD's other wave, in the middle of its step, issues first
     // (measured: +0.5%)
     __builtin_amdgcn_s_setprio(1);
-    issue_k(j + 4, kbuf(jm));
-    issue_v(j + 2, vbuf((jm + 2) & 3));
+    issue_k(j + 5, kbuf((jm + 1) & 3));
+    issue_v(j + 3, vbuf((jm + 3) & 3));
     const char* kt = kbuf((jm + 2) & 3);
     const char* vt = vbuf(jm);
 
@@ -644,8 +658,8 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
   auto step_any = [&](int j, f32x16* scur, f32x16* snext, u32x4* pcur, u32x4* pnext) __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD) : "memory");
     __syncthreads();
-    issue_k(j + 4, kbuf((j + 4) & 3));
-    issue_v(j + 2, vbuf((j + 2) & 3));
+    issue_k(j + 5, kbuf((j + 5) & 3));
+    issue_v(j + 3, vbuf((j + 3) & 3));
     if (j < nt_w) {
       const char* kt = kbuf((j + 2) & 3);
       const char* vt = vbuf(j & 3);
@@ -673,7 +687,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
   // ---- prologue: scores of tiles 0 and 1, P of tile 0
   f32x16 sa[KB], sb[KB];
   u32x4 pa[NU], pb[NU];
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NLD) : "memory");  // K 0, K 1 and K 2 have landed
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NLD) : "memory");  // K 0, K 1 and K 2 have landed
   __syncthreads();
   if (nt_w > 0) {
     // tile 0 from a zero reference; its row maximum becomes the reference.
@@ -703,6 +717,12 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
 #pragma unroll
     for (int i = 0; i < NPF; ++i) kpre[i] = k_frag(kbuf(2), i);
   }
+  // every wave's reads of K tile 0 were consumed by its prologue products:
+  // the stage can take K tile 4
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  issue_k(4, kbuf(0));
   for (; j < j_fast; j += 4) {
     step_fast(j, Int<0>{}, sb, sa, pa, pb);
     step_fast(j + 1, Int<1>{}, sa, sb, pb, pa);
