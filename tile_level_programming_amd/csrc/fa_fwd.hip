@@ -98,7 +98,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSumBound = 4096.0f;
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr int kWaves = 4;                       // waves per work-group
-constexpr int kBM = 32 * kWaves;                // queries per work-group
+constexpr int kBM = 32 * kWaves;                // queries per work-group (one key group)
 
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedValu = 0x002;
@@ -260,43 +260,55 @@ struct Flag { static constexpr bool value = B; };
 template <int I>
 struct Int { static constexpr int value = I; };
 
-template <int D, bool BF16, bool CAUSAL, int BN, bool SPLIT>
+// KG key groups of kWaves/KG waves each (1, or 2 for launches that leave
+// most CUs idle): group g takes the g-th share of the block's key tiles, the
+// groups' partial results are merged through LDS at the end, and a
+// work-group owns 32*kWaves/KG queries.  The longest block's work is then
+// spread over KG times as many work-groups, each SIMD doing 1/KG of it.
+template <int D, bool BF16, bool CAUSAL, int BN, bool SPLIT, int KG = 1>
 __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kernel(Params p) {
+  constexpr int WPG = kWaves / KG;                // waves per key group
+  constexpr int BM = 32 * WPG;                    // queries per work-group
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int ROWB = 2 * D;                     // bytes per row
   constexpr int TILE = BN * ROWB;                 // bytes of one K or V tile
-  constexpr int NLD = TILE / 16 / (64 * kWaves);  // load instructions per wave per tile
+  constexpr int NLD = TILE / 16 / (64 * WPG);     // load instructions per wave per tile
   constexpr int KB = BN / 32;                     // 32-key blocks per tile
   constexpr int NU = BN / 16;                     // 16-key slices per tile (P.V product steps)
   constexpr int DK = D / 16;                      // k-steps of the score product
   constexpr int DB = D / 32;                      // 32-wide d blocks of the output
   constexpr int NS = KB * DK;                     // score products per tile
   constexpr int NSA = NS / 2;                     // of which issued ahead of the row maximum
-  static_assert(TILE % (16 * 64 * kWaves) == 0, "tile must split evenly over the waves");
+  static_assert(TILE % (16 * 64 * WPG) == 0, "tile must split evenly over the waves");
+  static_assert(KG == 1 || (KG == 2 && !SPLIT), "two key groups only without a split over the keys");
   static_assert(DK >= NSA, "the early score products must share one 32-key block");
 
   // A ring of four LDS stages per tensor (tile t in stage t % 4), each a
   // separate array: the compiler can then tell that the loads streaming into
   // one stage never alias the reads from another.  Tiles are loaded two steps
   // before they are read, which hides the load latency of a step.
-  __shared__ u32x4 kst0[TILE / 16];
-  __shared__ u32x4 kst1[TILE / 16];
-  __shared__ u32x4 kst2[TILE / 16];
-  __shared__ u32x4 kst3[TILE / 16];
-  __shared__ u32x4 vst0[TILE / 16];
-  __shared__ u32x4 vst1[TILE / 16];
-  __shared__ u32x4 vst2[TILE / 16];
-  __shared__ u32x4 vst3[TILE / 16];
-  auto kbuf = [&](int t) __attribute__((always_inline)) -> char* {
-    return reinterpret_cast<char*>(t == 0 ? kst0 : t == 1 ? kst1 : t == 2 ? kst2 : kst3);
-  };
-  auto vbuf = [&](int t) __attribute__((always_inline)) -> char* {
-    return reinterpret_cast<char*>(t == 0 ? vst0 : t == 1 ? vst1 : t == 2 ? vst2 : vst3);
-  };
+  // (With two key groups each stage holds one tile per group.)
+  __shared__ u32x4 kst0[KG * TILE / 16];
+  __shared__ u32x4 kst1[KG * TILE / 16];
+  __shared__ u32x4 kst2[KG * TILE / 16];
+  __shared__ u32x4 kst3[KG * TILE / 16];
+  __shared__ u32x4 vst0[KG * TILE / 16];
+  __shared__ u32x4 vst1[KG * TILE / 16];
+  __shared__ u32x4 vst2[KG * TILE / 16];
+  __shared__ u32x4 vst3[KG * TILE / 16];
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave branches scalar
+  // the wave within its key group, and the group (uniform: keeps per-wave
+  // branches scalar)
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) % WPG);
+  const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane((tid >> 6) / WPG);
   const int lane = tid & 63;
+  auto kbuf = [&](int t) __attribute__((always_inline)) -> char* {
+    return reinterpret_cast<char*>(t == 0 ? kst0 : t == 1 ? kst1 : t == 2 ? kst2 : kst3) + grp * TILE;
+  };
+  auto vbuf = [&](int t) __attribute__((always_inline)) -> char* {
+    return reinterpret_cast<char*>(t == 0 ? vst0 : t == 1 ? vst1 : t == 2 ? vst2 : vst3) + grp * TILE;
+  };
   const int n = lane & 31;  // query column owned by this lane
   const int h = lane >> 5;  // which half of the wave
 
@@ -321,14 +333,17 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     bh = SPLIT ? t2 / p.n_split : t2;
     if (CAUSAL) qblk = p.n_qblk - 1 - qblk;  // longest blocks first
   }
-  const int q0 = qblk * kBM;
+  const int q0 = qblk * BM;
   const int qw0 = q0 + wave * 32;  // first query of this wave
   const int qi = qw0 + n;          // query of this lane
 
-  // the keys of this block: all of them, or (split) the Skl keys from kb0 on;
-  // tiles, masks and loads count keys from kb0
-  const int kb0 = SPLIT ? split * p.kchunk : 0;
-  const int Skl = SPLIT ? min(p.Sk - kb0, p.kchunk) : p.Sk;
+  // the keys of this block: all of them, or (split) the Skl keys from kb0 on,
+  // or (two key groups) group g's share of the block's key tiles, tpg tiles
+  // from tile g*tpg on; tiles, masks and loads count keys from kb0
+  const int kend0 = CAUSAL ? min(p.Sk, q0 + BM) : p.Sk;  // (two key groups) the block's keys
+  const int tpg = KG == 1 ? 0 : ((kend0 + BN - 1) / BN + KG - 1) / KG;
+  const int kb0 = SPLIT ? split * p.kchunk : KG == 1 ? 0 : grp * tpg * BN;
+  const int Skl = SPLIT ? min(p.Sk - kb0, p.kchunk) : KG == 1 ? p.Sk : max(0, min(p.Sk - kb0, tpg * BN));
   const int qw0r = qw0 - kb0;  // query positions relative to kb0 (the causal
   const int qir = qi - kb0;    // mask compares them with key positions)
 
@@ -336,8 +351,10 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
   const uint16_t* kg = p.k + ((size_t)bh * p.Sk + kb0) * D;
   const uint16_t* vg = p.v + ((size_t)bh * p.Sk + kb0) * D;
 
-  const int kend = CAUSAL ? min(Skl, q0 - kb0 + kBM) : Skl;  // (split, causal: may be <= 0)
+  const int kend = CAUSAL ? min(Skl, q0 - kb0 + BM) : Skl;  // (split, key groups, causal: may be <= 0)
   const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // steps of every wave of the work-group (each step has one barrier)
+  const int nsteps = KG == 1 ? ntiles : tpg;
   // tiles this wave computes: all of the work-group's, less (causal) those
   // wholly above its last query; none for waves past the last query
   int nt_w = CAUSAL ? (qw0r + 31 < 0 ? 0 : min(ntiles, (qw0r + 31) / BN + 1)) : ntiles;
@@ -356,7 +373,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
   int offk[NLD], offv[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    const int slot = (i * kWaves + wave) * 64 + lane;  // 16-byte slot within the tile
+    const int slot = (i * WPG + wave) * 64 + lane;  // 16-byte slot within the tile
     const int r = slot / CH, pc = slot % CH;
     offk[i] = r * ROWB + ((pc ^ ksw<D>(r)) << 4);
     offv[i] = r * ROWB + ((pc ^ vsw<D>(r)) << 4);
@@ -366,10 +383,10 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, (uint32_t)Skl * ROWB, kBufferWord3);
   auto issue_k = [&](int tile, char* buf) __attribute__((always_inline)) {
-    load_rows_to_lds<NLD>(rk, tile * BN, ROWB, buf + wave * 1024, kWaves * 1024, offk);
+    load_rows_to_lds<NLD>(rk, tile * BN, ROWB, buf + wave * 1024, WPG * 1024, offk);
   };
   auto issue_v = [&](int tile, char* buf) __attribute__((always_inline)) {
-    load_rows_to_lds<NLD>(rv, tile * BN, ROWB, buf + wave * 1024, kWaves * 1024, offv);
+    load_rows_to_lds<NLD>(rv, tile * BN, ROWB, buf + wave * 1024, WPG * 1024, offv);
   };
 
   // Tile t of K lands two steps before its fragments are read (at the end of
@@ -698,7 +715,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     score_tile(sa, kbuf(0));
     apply_mask(sa, 0);
     m_ref = tile_max(sa);
-    if (SPLIT && CAUSAL && m_ref == -INFINITY) m_ref = 0.f;
+    if ((SPLIT || KG > 1) && CAUSAL && m_ref == -INFINITY) m_ref = 0.f;
     set_negm();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -730,14 +747,52 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     step_fast(j + 3, Int<3>{}, sa, sb, pb, pa);
   }
   // (j is a multiple of 4 here)
-  for (; j < ntiles; j += 2) {
+  for (; j < nsteps; j += 2) {
     step_any(j, sb, sa, pa, pb);
-    if (j + 1 < ntiles) step_any(j + 1, sa, sb, pb, pa);
+    if (j + 1 < nsteps) step_any(j + 1, sa, sb, pb, pa);
   }
 
   // the last steps' loads (past the keys) are still in flight: let them land
   // before the work-group's LDS can be handed to another
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if constexpr (KG == 2) {
+    // Group 1 hands its partial result to group 0 through LDS (the K stages
+    // hold O, one wave per stage; the V stages m, l and the rounding
+    // correction).  Both partials are against their own reference: with M
+    // the larger, each is rescaled by 2^(c (m_g - M)), the online softmax's
+    // own rescaling.  A group that saw no key of a row has l = 0 and weighs
+    // nothing; a NaN row stays NaN.
+    float* ob = reinterpret_cast<float*>(wave == 0 ? kst0 : wave == 1 ? kst1 : wave == 2 ? kst2 : kst3);
+    float* mb = reinterpret_cast<float*>(wave == 0 ? vst0 : wave == 1 ? vst1 : wave == 2 ? vst2 : vst3);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave is done with the tiles
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ob[(db * 16 + r) * 64 + lane] = oacc[db][r];
+      mb[lane] = m_ref;
+      mb[64 + lane] = l_run;
+      mb[128 + lane] = l_corr;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 1) return;
+    const float m1 = mb[lane], l1 = mb[64 + lane], c1 = mb[128 + lane];
+    const float mm = l1 == 0.f ? m_ref : __builtin_elementwise_maximum(m_ref, m1);
+    const float a0 = exp2f((m_ref - mm) * c);
+    const float a1 = l1 == 0.f ? 0.f : exp2f((m1 - mm) * c);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + ob[(db * 16 + r) * 64 + lane] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    l_corr = l_corr * a0 + c1 * a1;
+    m_ref = mm;
+  }
 
   // ---- epilogue: normalise, round, store O rows and lse
   if (SPLIT && qi < p.Sq) {
@@ -785,8 +840,13 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
 // (measured about 2% faster than 64-key tiles with two); a launch of at most
 // kSmallGrid work-groups, which runs as a single wave of work-groups, takes
 // 64-key tiles: half the steps per work-group, and its latency is the
-// launch's (measured 6% faster on 128 work-groups).
+// launch's (measured 6% faster on 128 work-groups).  A launch of at most
+// kHalfGrid work-groups (no split over the keys) would leave half of the CUs
+// idle and last as long as its longest block's work on one CU: it runs with
+// two key groups of two waves instead, 64 queries per work-group, so that
+// twice as many work-groups each do half of a block's keys.
 constexpr int64_t kSmallGrid = 512;
+constexpr int64_t kHalfGrid = 128;
 
 template <int D, bool BF16, bool CAUSAL, bool SPLIT>
 hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream) {
@@ -799,6 +859,13 @@ hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream
     if (p.n_wg <= kSmallGrid) {
       fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, 64, SPLIT>);
       per_cu = 2;
+    }
+  if constexpr (!SPLIT)
+    if (p.n_wg <= kHalfGrid) {
+      fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, D == 64 ? 64 : 32, SPLIT, 2>);
+      per_cu = 1;
+      p.n_qblk = (int)((Sq + kBM / 2 - 1) / (kBM / 2));
+      p.n_wg = (int)(BH * p.n_qblk);
     }
   // Causal blocks run longest first across an XCD's heads when a head has
   // fewer query blocks than the XCD (32 CUs) has work-group slots: head by
