@@ -274,7 +274,10 @@ def fwd_split(q, k, v, causal: bool = False, scale: float | None = None, n_split
     need = split_workspace_size(B, H, Sq, Sk, D, n_split)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check_out(workspace, "workspace", (workspace.numel(),), workspace.dtype, q.device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or workspace.device != q.device:
+        raise ValueError(f"workspace must be a tensor on {q.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     dt = FA_F16 if q.dtype == torch.float16 else FA_BF16
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
