@@ -40,7 +40,7 @@ extern "C" {
  *       written, rounded to nearest even from the fp32 result.
  * M, N, K >= 1; K must be a multiple of 8 (rows of 16-byte chunks),
  *       otherwise FA_ERR_UNSUPPORTED.  M, N, K < 2^31, 256*K < 2^32 - 16,
- *       and ceil(M/128)*ceil(N/128) < 2^31.
+ *       and ceil(M/256)*ceil(N/256) < 2^31.
  * dtype FA_F16 or FA_BF16.
  * stream a hipStream_t (NULL = the null stream).
  *

@@ -13,34 +13,39 @@
 // A [M, K], W [N, K] (the weight layout of a linear layer), bias [N] and C
 // [M, N], row-major, fp16 or bf16, accumulation in fp32.
 //
-// CDNA4 mapping.  One work-group of eight waves (two per SIMD) owns a
-// 256 x 256 tile of C; the waves form a 4 (n) x 2 (m) grid, each owning 64
-// columns n by 128 rows m as 2 x 4 blocks of v_mfma_f32_32x32x16 (128
+// CDNA4 mapping.  One work-group of four waves (one per SIMD) owns a
+// 256 x 256 tile of C; the waves form a 2 (n) x 2 (m) grid, each owning 128
+// columns n by 128 rows m as 4 x 4 blocks of v_mfma_f32_32x32x16 (256
 // accumulator registers).  The products are formed transposed, C^T = W A^T:
 // the W fragment is the A operand and the A fragment the B operand, so a
 // lane owns one row m of C and holds 16 of its columns n per block in runs
 // of 4 consecutive ones (8-byte stores in the epilogue).  Both fragments are
 // 16-byte reads of K-contiguous rows.
 //
-//  * K is streamed in 32-wide slabs through a ring of four LDS stages (A and
-//    W slab of a stage: 16 KiB each, 128 KiB in all), loaded three slabs
-//    ahead with buffer_load_dwordx4 straight into LDS.  Each lane picks the
-//    global 16-byte chunk that belongs at its LDS slot, which lays a row's
-//    four chunks out XOR-swizzled (chunk c of row r at c ^ ((r >> 2) & 3)):
-//    the fragment reads of 16 consecutive rows then hit all 64 banks once.
-//    The first k-step's fragments of the next slab are read during each
-//    step, between its last products, so a step's products start without
-//    waiting for LDS; a step issues its loads, then its remaining fragment
-//    reads, then its products.
+//  * K is streamed in 64-wide slabs through two LDS stages (A and W slab of
+//    a stage: 32 KiB each, 128 KiB in all) with buffer_load_dwordx4 straight
+//    into LDS.  A slab row is one 128-byte line of A or W, so every load
+//    instruction fetches whole lines.  Each lane picks the global 16-byte
+//    chunk that belongs at its LDS slot, which lays a row's eight chunks out
+//    XOR-swizzled (chunk c of row r at c ^ ((r >> 1) & 7)): the fragment
+//    reads of 16 consecutive rows then hit all 64 banks once.
+//  * A step computes one slab in four k-steps of 16, reading each k-step's
+//    fragments during the previous one's products.  Halfway through the last
+//    k-step every wave waits for the next slab's loads and meets the others
+//    at a barrier; the remaining products then cover the first fragment
+//    reads of the next slab, and the slab's own stage, now read by every
+//    wave, takes the loads of the slab after next.  Those loads are spread:
+//    a few between the step's last products, the rest between the next
+//    step's first k-step products, so that the address unit is never flooded
+//    and the later ones still land a k-step before they are needed.
 //  * Rows past M or N lie outside the buffer range and read as zeros;
 //    chunks past K get an offset outside the range and read as zeros.
-//    Slabs past the end are loaded as zeros too, so every wait has a fixed
-//    count.
+//    Slabs past the end are loaded as zeros too.
 //  * Work-group ids are remapped so that each XCD runs a contiguous range of
 //    tiles, ordered in groups of 4 tile rows (column-major inside a group):
 //    the 32 tiles an XCD runs together are 4 rows by 8 columns of tiles, and
 //    share rows of A and W in its L2.
-//  * Epilogue: acc + bias[n] (read before the K loop), gelu in fp32 with the
+//  * Epilogue: acc + bias[n] (read after the K loop), gelu in fp32 with the
 //    Abramowitz-Stegun erf approximation, rounded to nearest even.
 
 #include <hip/hip_runtime.h>
@@ -65,15 +70,26 @@ constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // a buffer offset past any rang
 constexpr int kGroupM = 4;                      // tile rows per ordering group
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmem = 0x010;
 constexpr int kSchedDsRead = 0x100;
 
-// Tile configuration: a work-group of WGN x WGM waves (n x m), each wave
-// owning WTN x WTM blocks of 32 x 32; K is streamed in BK-wide slabs through
-// NST LDS stages, loaded NST-1 slabs ahead.
-struct Cfg {
-  static constexpr int WGN = 4, WGM = 2, WTN = 2, WTM = 4, BK = 32, NST = 4;
-  static constexpr int BN = 32 * WTN * WGN, BM = 32 * WTM * WGM, NW = WGN * WGM;
-};
+// Tile configuration: four waves in a 2 (n) x 2 (m) grid, each owning
+// 4 x 4 blocks of 32 x 32 of a 256 x 256 tile; K in 64-wide slabs, two
+// LDS stages.
+constexpr int kWaves = 4;
+constexpr int WT = 128;                    // wave-tile edge
+constexpr int NB = WT / 32;                // 32 x 32 blocks per wave-tile edge
+constexpr int BM = 256, BN = 256;          // tile of C per work-group
+constexpr int BK = 64;                     // slab width: one 128-byte line per row
+constexpr int ROWB = BK * 2;               // bytes of a slab row
+constexpr int CPR = BK / 8;                // 16-byte chunks per slab row
+constexpr int SLAB = 256 * ROWB;           // bytes of one matrix's slab
+constexpr int NLA = SLAB / (16 * 64 * kWaves);  // loads per wave and matrix per slab
+constexpr int NL = 2 * NLA;                // loads per wave per slab (A first, then W)
+constexpr int KS = BK / 16;                // k-steps per slab
+constexpr int NL1 = 4;                     // loads of a slab issued before the next step
+static_assert(NLA * 16 * 64 * kWaves == SLAB, "slabs split over the waves");
+static_assert(KS == 4, "the step is written for four k-steps");
 
 struct GemmParams {
   const uint16_t* a;
@@ -158,35 +174,21 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   return base + local;
 }
 
-template <bool BF16, int WGN, int WGM, int WTN, int WTM, int BK, int NST>
-__global__ __launch_bounds__(64 * WGN * WGM) void gemm_bias_gelu_kernel(GemmParams p) {
-  constexpr int kWaves = WGN * WGM;
-  constexpr int BN = 32 * WTN * WGN, BM = 32 * WTM * WGM;
-  constexpr int ROWB = BK * 2;                 // bytes of a slab row
-  constexpr int CPR = BK / 8;                  // 16-byte chunks per slab row
-  constexpr int RPL = 256 / ROWB;              // slab rows per 256-byte bank line
-  constexpr int ASLAB = BM * ROWB, WSLAB = BN * ROWB;
-  constexpr int NLA = ASLAB / (16 * 64 * kWaves), NLW = WSLAB / (16 * 64 * kWaves);  // loads per wave
-  static_assert(NST >= 3 && NST <= 4, "three or four stages");
-  static_assert(NLA * 16 * 64 * kWaves == ASLAB && NLW * 16 * 64 * kWaves == WSLAB, "slabs split over the waves");
+template <bool BF16>
+__global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmParams p) {
   // one array per stage and matrix: the compiler can then tell that the
-  // loads streaming into one stage never alias the reads from another
-  __shared__ u32x4 as0[ASLAB / 16], as1[ASLAB / 16], as2[NST > 2 ? ASLAB / 16 : 1], as3[NST > 3 ? ASLAB / 16 : 1];
-  __shared__ u32x4 ws0[WSLAB / 16], ws1[WSLAB / 16], ws2[NST > 2 ? WSLAB / 16 : 1], ws3[NST > 3 ? WSLAB / 16 : 1];
-  auto abuf = [&](int s) __attribute__((always_inline)) -> char* {
-    return reinterpret_cast<char*>(s == 0 ? as0 : s == 1 ? as1 : s == 2 ? as2 : as3);
-  };
-  auto wbuf = [&](int s) __attribute__((always_inline)) -> char* {
-    return reinterpret_cast<char*>(s == 0 ? ws0 : s == 1 ? ws1 : s == 2 ? ws2 : ws3);
-  };
+  // loads streaming into one stage never alias the reads from the other
+  __shared__ u32x4 as0[SLAB / 16], as1[SLAB / 16], ws0[SLAB / 16], ws1[SLAB / 16];
+  auto abuf = [&](int s) __attribute__((always_inline)) -> char* { return reinterpret_cast<char*>(s == 0 ? as0 : as1); };
+  auto wbuf = [&](int s) __attribute__((always_inline)) -> char* { return reinterpret_cast<char*>(s == 0 ? ws0 : ws1); };
   // chunk c of slab row r sits at physical chunk c ^ swz(r): the 16-byte
   // fragment reads of 16 consecutive rows then cover all 64 banks once
-  auto swz = [](int r) __attribute__((always_inline)) { return (r / RPL) & (CPR - 1); };
+  auto swz = [](int r) __attribute__((always_inline)) { return (r >> 1) & (CPR - 1); };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave % WGM, wn = wave / WGM;  // this wave's part of the tile
+  const int wm = wave & 1, wn = wave >> 1;  // this wave's part of the tile
 
   // tile of this work-group: groups of kGroupM tile rows, column-major inside
   const int t = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
@@ -206,41 +208,35 @@ __global__ __launch_bounds__(64 * WGN * WGM) void gemm_bias_gelu_kernel(GemmPara
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.w + (size_t)n0 * p.K), (short)0, (uint32_t)min(BN, p.N - n0) * rowg, kBufferWord3);
 
-  // load slots: instruction i of this wave fills 1 KiB block i*4 + wave of a
-  // slab; lane l writes bytes 16l..16l+15 of it: row slot / CPR, physical
-  // chunk slot % CPR, which holds logical chunk pc ^ swz(row)
-  uint32_t arow[NLA], wrow[NLW];
-  int ak[NLA], wk[NLW];
+  // load slots: load i of a matrix fills 1 KiB block i * kWaves + wave of
+  // its slab; lane l writes bytes 16l .. 16l + 15 of it: row slot / CPR,
+  // physical chunk slot % CPR, which holds logical chunk pc ^ swz(row).
+  // The slots are the same for A and W.
+  uint32_t lrow[NLA];
+  int lk[NLA];
 #pragma unroll
   for (int i = 0; i < NLA; ++i) {
     const int slot = (i * kWaves + wave) * 64 + lane;
     const int row = slot / CPR;
-    arow[i] = (uint32_t)row * rowg;
-    ak[i] = ((slot % CPR) ^ swz(row)) * 8;
+    lrow[i] = (uint32_t)row * rowg;
+    lk[i] = ((slot % CPR) ^ swz(row)) * 8;
   }
-#pragma unroll
-  for (int i = 0; i < NLW; ++i) {
-    const int slot = (i * kWaves + wave) * 64 + lane;
-    const int row = slot / CPR;
-    wrow[i] = (uint32_t)row * rowg;
-    wk[i] = ((slot % CPR) ^ swz(row)) * 8;
-  }
-  auto issue = [&](int slab, int stage) __attribute__((always_inline)) {
+  // loads I0 .. I1-1 of slab `slab` into `stage` (A's for q < NLA, then W's)
+  auto issue = [&](int slab, int stage, auto i0_tag, auto i1_tag) __attribute__((always_inline)) {
+    constexpr int I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value;
     const int k0 = slab * BK;
-#pragma unroll
-    for (int i = 0; i < NLA; ++i) {
-      const int k = k0 + ak[i];
-      const uint32_t off = k < p.K ? arow[i] + (uint32_t)k * 2u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(abuf(stage) + (i * kWaves + wave) * 1024), 16, off,
-                                               0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NLW; ++i) {
-      const int k = k0 + wk[i];
-      const uint32_t off = k < p.K ? wrow[i] + (uint32_t)k * 2u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(wbuf(stage) + (i * kWaves + wave) * 1024), 16, off,
-                                               0, 0, 0);
-    }
+    static_for<I0, I1>([&](auto it) {
+      constexpr int q = decltype(it)::value;
+      constexpr int i = q % NLA;
+      const int k = k0 + lk[i];
+      const uint32_t off = k < p.K ? lrow[i] + (uint32_t)k * 2u : kOutOfRange;
+      if constexpr (q < NLA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(abuf(stage) + (i * kWaves + wave) * 1024), 16, off,
+                                                 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(wbuf(stage) + (i * kWaves + wave) * 1024), 16, off,
+                                                 0, 0, 0);
+    });
   };
 
   // fragment of block row0.. (32 rows), k-step s (16 wide) of a slab: lane l
@@ -251,85 +247,113 @@ __global__ __launch_bounds__(64 * WGN * WGM) void gemm_bias_gelu_kernel(GemmPara
     const int pc = (2 * s + fh) ^ swz(r);
     return *reinterpret_cast<const u32x4*>(base + r * ROWB + pc * 16);
   };
-
-  f32x16 acc[WTN][WTM];
+  // the fragments of k-step s, in the order the products use them
+  auto read = [&](u32x4* wf, u32x4* af, const char* wt, const char* at, int s) __attribute__((always_inline)) {
+    wf[0] = frag(wt, wn * WT, s);
 #pragma unroll
-  for (int i = 0; i < WTN; ++i)
+    for (int b = 0; b < NB; ++b) af[b] = frag(at, wm * WT + b * 32, s);
 #pragma unroll
-    for (int j = 0; j < WTM; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // the fragments of k-step 0 of the next slab, read at the end of a step
-  u32x4 wpre[WTN], apre[WTM];
-  auto read_pre = [&](int stage) __attribute__((always_inline)) {
-#pragma unroll
-    for (int b = 0; b < WTN; ++b) wpre[b] = frag(wbuf(stage), wn * 32 * WTN + b * 32, 0);
-#pragma unroll
-    for (int b = 0; b < WTM; ++b) apre[b] = frag(abuf(stage), wm * 32 * WTM + b * 32, 0);
+    for (int b = 1; b < NB; ++b) wf[b] = frag(wt, wn * WT + b * 32, s);
   };
 
-  // step j (slab j in stage j % NST, passed at compile time as ST)
+  f32x16 acc[NB][NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // products of block rows bn0 .. bn1-1 with one k-step's fragments
+  auto mm = [&](const u32x4* wf, const u32x4* af, int bn0, int bn1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int bn = bn0; bn < bn1; ++bn)
+#pragma unroll
+      for (int bm = 0; bm < NB; ++bm) acc[bn][bm] = mfma_32x32x16<BF16>(wf[bn], af[bm], acc[bn][bm]);
+  };
+
+  constexpr int NF = 2 * NB;  // fragment reads per k-step
+  constexpr int NM = NB * NB;  // products per k-step
+  constexpr int NH = NM / 2;
+  constexpr int NL2 = NL - NL1;
+  // one fragment read after every other product of a k-step
+  auto spread_reads = [&]() __attribute__((always_inline)) {
+    static_for<0, NM>([&](auto it) {
+      constexpr int i = decltype(it)::value;
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if constexpr (i % 2 == 1 && i / 2 < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    });
+  };
+  u32x4 w0[NB], a0[NB], w1[NB], a1[NB];
+
+  // step j: slab j in stage ST (passed at compile time).  On entry the
+  // k-step-0 fragments of slab j are in w0/a0 and the first NL1 loads of
+  // slab j+1 are in flight.
   auto step = [&](int j, auto st_tag) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_tag)::value;
-    // slabs j and j+1 have landed once at most the NST-3 later slabs' loads
-    // are in flight; the barrier makes every wave's part of them visible
-    // (slab j+1 is read at the end of this step), and tells that every wave
-    // has finished reading the stage of slab j-1 (its fragments were all
-    // consumed by the previous steps' products), which slab j+NST-1 now
-    // overwrites.  Slabs past the end are zeros and may be read.
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 3) * (NLA + NLW)) : "memory");
-    issue(j + NST - 1, (ST + NST - 1) % NST);
-    // the loads go out first: nothing of the step may be scheduled above them
-    __builtin_amdgcn_sched_barrier(0);
     const char* at = abuf(ST);
     const char* wt = wbuf(ST);
-    u32x4 wf[BK / 16][WTN], af[BK / 16][WTM];
-#pragma unroll
-    for (int b = 0; b < WTN; ++b) wf[0][b] = wpre[b];
-#pragma unroll
-    for (int b = 0; b < WTM; ++b) af[0][b] = apre[b];
-#pragma unroll
-    for (int s = 1; s < BK / 16; ++s) {
-#pragma unroll
-      for (int b = 0; b < WTN; ++b) wf[s][b] = frag(wt, wn * 32 * WTN + b * 32, s);
-#pragma unroll
-      for (int b = 0; b < WTM; ++b) af[s][b] = frag(at, wm * 32 * WTM + b * 32, s);
-    }
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s)
-#pragma unroll
-      for (int bn = 0; bn < WTN; ++bn)
-#pragma unroll
-        for (int bm = 0; bm < WTM; ++bm) acc[bn][bm] = mfma_32x32x16<BF16>(wf[s][bn], af[s][bm], acc[bn][bm]);
-    read_pre((ST + 1) % NST);
-    // the fragments of the later k-steps first, then the k-step-0 products,
-    // then the later products with the next slab's first fragments read
-    // between them (measured: +11% on 8192 x 16384 x 4096)
-    constexpr int NF = WTN + WTM, NM = WTN * WTM;
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NF * (BK / 16 - 1), 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, NM, 0);
-#pragma unroll
-    for (int i = 0; i < NF; ++i) {
+    // k-step 0, with the k-step-1 reads and the rest of slab j+1's loads
+    issue(j + 1, ST ^ 1, Int<NL1>{}, Int<NL>{});
+    read(w1, a1, wt, at, 1);
+    mm(w0, a0, 0, NB);
+    static_for<0, NM>([&](auto it) {
+      constexpr int i = decltype(it)::value;
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, NM * (BK / 16 - 1) - NF, 0);
+      if constexpr (i % 2 == 1 && i / 2 < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if constexpr (i * NL2 / NM != (i + 1) * NL2 / NM) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
+    });
+    read(w0, a0, wt, at, 2);
+    mm(w1, a1, 0, NB);
+    spread_reads();
+    read(w1, a1, wt, at, 3);
+    mm(w0, a0, 0, NB);
+    spread_reads();
+    // k-step 3: half of the products, then the wait for slab j+1 (the only
+    // loads in flight: every later slab is issued after this point) and the
+    // barrier after which every wave has read all of slab j, whose stage
+    // then takes the first loads of slab j+2
+    mm(w1, a1, 0, NB / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    read(w0, a0, wbuf(ST ^ 1), abuf(ST ^ 1), 0);
+    issue(j + 2, ST, Int<0>{}, Int<NL1>{});
+    mm(w1, a1, NB / 2, NB);
+    static_for<0, NH>([&](auto it) {
+      constexpr int i = decltype(it)::value;
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if constexpr (i < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if constexpr (i * NL1 / NH != (i + 1) * NL1 / NH)
+        __builtin_amdgcn_sched_group_barrier(kSchedVmem, (i + 1) * NL1 / NH - i * NL1 / NH, 0);
+    });
   };
 
   const int nk = (p.K + BK - 1) / BK;
-  static_for<0, NST - 1>([&](auto it) { issue(it.value, it.value); });
+  issue(0, 0, Int<0>{}, Int<NL>{});
+  issue(1, 1, Int<0>{}, Int<NL1>{});
+  // slab 0 has landed once only slab 1's first loads are in flight
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NL1) : "memory");
+  read(w0, a0, wbuf(0), abuf(0), 0);
+  int j = 0;
+  for (; j + 2 <= nk; j += 2) {
+    step(j, Int<0>{});
+    step(j + 1, Int<1>{});
+  }
+  if (j < nk) step(j, Int<0>{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // the bias of the lane's columns n0 + 32(WTN wn + bn) + 8g + 4(l/32) + 0..3,
-  // read before the loop (8-byte loads where aligned and inside N)
-  u32x2 bias_pk[WTN][4];
+  // epilogue: lane holds C[m][n] for m = m0 + 128 wm + 32 bm + l%32 and
+  // n = n0 + 128 wn + 32 bn + 8g + 4(l/32) + e (accumulator slot 4g + e);
+  // the bias of those columns is read now (8-byte loads where aligned and
+  // inside N)
+  u32x2 bias_pk[NB][4];
   {
     const bool bvec = ((uintptr_t)p.bias & 7u) == 0;
 #pragma unroll
-    for (int bn = 0; bn < WTN; ++bn)
+    for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int nb = n0 + (wn * WTN + bn) * 32 + 8 * g + 4 * fh;
+        const int nb = n0 + wn * WT + bn * 32 + 8 * g + 4 * fh;
         u32x2 v = {0u, 0u};
         if (p.bias) {
           if (bvec && nb + 3 < p.N) {
@@ -345,29 +369,17 @@ __global__ __launch_bounds__(64 * WGN * WGM) void gemm_bias_gelu_kernel(GemmPara
         bias_pk[bn][g] = v;
       }
   }
-  // slab 0 has landed once the NST-2 later slabs' loads are in flight
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 2) * (NLA + NLW)) : "memory");
-  read_pre(0);
-  int j = 0;
-  for (; j + NST <= nk; j += NST) static_for<0, NST>([&](auto it) { step(j + it.value, it); });
-  static_for<0, NST - 1>([&](auto it) {
-    if (j + it.value < nk) step(j + it.value, it);
-  });
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // epilogue: lane holds C[m][n] for m = m0 + 32(WTM wm + bm) + l%32 and
-  // n = n0 + 32(WTN wn + bn) + 8g + 4(l/32) + e (accumulator slot 4g + e)
   const bool vec = (p.N & 3) == 0;
 #pragma unroll
-  for (int bm = 0; bm < WTM; ++bm) {
-    const int m = m0 + (wm * WTM + bm) * 32 + fr;
+  for (int bm = 0; bm < NB; ++bm) {
+    const int m = m0 + wm * WT + bm * 32 + fr;
     if (m >= p.M) continue;
     uint16_t* crow = p.c + (size_t)m * p.N;
 #pragma unroll
-    for (int bn = 0; bn < WTN; ++bn)
+    for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int nb = n0 + (wn * WTN + bn) * 32 + 8 * g + 4 * fh;
+        const int nb = n0 + wn * WT + bn * 32 + 8 * g + 4 * fh;
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -408,7 +420,7 @@ extern "C" fa_status gemm_bias_gelu(const void* a, const void* w, const void* bi
   // a work-group's buffer range (up to 256 rows of 2K bytes) and the tile
   // count stay inside 32 bits
   if ((int64_t)256 * K * 2 >= (int64_t)kOutOfRange) return FA_ERR_INVALID_ARG;
-  const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM, tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   if (tiles_m * tiles_n >= lim) return FA_ERR_INVALID_ARG;
   const size_t a_bytes = (size_t)M * (size_t)K * 2, w_bytes = (size_t)N * (size_t)K * 2;
   const size_t c_bytes = (size_t)M * (size_t)N * 2, b_bytes = (size_t)N * 2;
@@ -427,13 +439,9 @@ extern "C" fa_status gemm_bias_gelu(const void* a, const void* w, const void* bi
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   void* args[] = {&p};
-  const void* fn =
-      dtype == FA_BF16
-          ? reinterpret_cast<const void*>(
-                &gemm_bias_gelu_kernel<true, Cfg::WGN, Cfg::WGM, Cfg::WTN, Cfg::WTM, Cfg::BK, Cfg::NST>)
-          : reinterpret_cast<const void*>(
-                &gemm_bias_gelu_kernel<false, Cfg::WGN, Cfg::WGM, Cfg::WTN, Cfg::WTM, Cfg::BK, Cfg::NST>);
-  const hipError_t err = hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * Cfg::NW), args, 0,
+  const void* fn = dtype == FA_BF16 ? reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<true>)
+                                    : reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<false>);
+  const hipError_t err = hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kWaves), args, 0,
                                          static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
