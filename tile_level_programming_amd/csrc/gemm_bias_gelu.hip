@@ -22,22 +22,23 @@
 // of 4 consecutive ones (8-byte stores in the epilogue).  Both fragments are
 // 16-byte reads of K-contiguous rows.
 //
-//  * K is streamed in 64-wide slabs through two LDS stages (A and W slab of
-//    a stage: 32 KiB each, 128 KiB in all) with buffer_load_dwordx4 straight
-//    into LDS.  A slab row is one 128-byte line of A or W, so every load
-//    instruction fetches whole lines.  Each lane picks the global 16-byte
-//    chunk that belongs at its LDS slot, which lays a row's eight chunks out
-//    XOR-swizzled (chunk c of row r at c ^ ((r >> 1) & 7)): the fragment
-//    reads of 16 consecutive rows then hit all 64 banks once.
+//  * K is streamed in 64-wide slabs with buffer_load_dwordx4 straight into
+//    LDS: A through two stages, W through three (32 KiB per slab and
+//    matrix, 160 KiB in all).  A slab row is one 128-byte line of A or W, so
+//    every load instruction fetches whole lines.  Each lane picks the global
+//    16-byte chunk that belongs at its LDS slot, which lays a row's eight
+//    chunks out XOR-swizzled (chunk c of row r at c ^ ((r >> 1) & 7)): the
+//    fragment reads of 16 consecutive rows then hit all 64 banks once.
 //  * A step computes one slab in four k-steps of 16, reading each k-step's
 //    fragments during the previous one's products.  Halfway through the last
 //    k-step every wave waits for the next slab's loads and meets the others
 //    at a barrier; the remaining products then cover the first fragment
-//    reads of the next slab, and the slab's own stage, now read by every
-//    wave, takes the loads of the slab after next.  Those loads are spread:
-//    a few between the step's last products, the rest between the next
-//    step's first k-step products, so that the address unit is never flooded
-//    and the later ones still land a k-step before they are needed.
+//    reads of the next slab.  The loads are spread over the products so
+//    that the address unit is never flooded: A slab j+2 goes into the stage
+//    A slab j leaves at that barrier, two loads right after it and the rest
+//    during the next step's first k-step; W slab j+2 goes into the third W
+//    stage during the middle k-steps of step j, a whole step before it is
+//    needed.
 //  * Rows past M or N lie outside the buffer range and read as zeros;
 //    chunks past K get an offset outside the range and read as zeros.
 //    Slabs past the end are loaded as zeros too.
@@ -74,8 +75,8 @@ constexpr int kSchedVmem = 0x010;
 constexpr int kSchedDsRead = 0x100;
 
 // Tile configuration: four waves in a 2 (n) x 2 (m) grid, each owning
-// 4 x 4 blocks of 32 x 32 of a 256 x 256 tile; K in 64-wide slabs, two
-// LDS stages.
+// 4 x 4 blocks of 32 x 32 of a 256 x 256 tile; K in 64-wide slabs, two LDS
+// stages for A and three for W.
 constexpr int kWaves = 4;
 constexpr int WT = 128;                    // wave-tile edge
 constexpr int NB = WT / 32;                // 32 x 32 blocks per wave-tile edge
@@ -87,7 +88,6 @@ constexpr int SLAB = 256 * ROWB;           // bytes of one matrix's slab
 constexpr int NLA = SLAB / (16 * 64 * kWaves);  // loads per wave and matrix per slab
 constexpr int NL = 2 * NLA;                // loads per wave per slab (A first, then W)
 constexpr int KS = BK / 16;                // k-steps per slab
-constexpr int NL1 = 4;                     // loads of a slab issued before the next step
 static_assert(NLA * 16 * 64 * kWaves == SLAB, "slabs split over the waves");
 static_assert(KS == 4, "the step is written for four k-steps");
 
@@ -177,10 +177,10 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
 template <bool BF16>
 __global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmParams p) {
   // one array per stage and matrix: the compiler can then tell that the
-  // loads streaming into one stage never alias the reads from the other
-  __shared__ u32x4 as0[SLAB / 16], as1[SLAB / 16], ws0[SLAB / 16], ws1[SLAB / 16];
+  // loads streaming into one stage never alias the reads from another
+  __shared__ u32x4 as0[SLAB / 16], as1[SLAB / 16], ws0[SLAB / 16], ws1[SLAB / 16], ws2[SLAB / 16];
   auto abuf = [&](int s) __attribute__((always_inline)) -> char* { return reinterpret_cast<char*>(s == 0 ? as0 : as1); };
-  auto wbuf = [&](int s) __attribute__((always_inline)) -> char* { return reinterpret_cast<char*>(s == 0 ? ws0 : ws1); };
+  auto wbuf = [&](int s) __attribute__((always_inline)) -> char* { return reinterpret_cast<char*>(s == 0 ? ws0 : s == 1 ? ws1 : ws2); };
   // chunk c of slab row r sits at physical chunk c ^ swz(r): the 16-byte
   // fragment reads of 16 consecutive rows then cover all 64 banks once
   auto swz = [](int r) __attribute__((always_inline)) { return (r >> 1) & (CPR - 1); };
@@ -221,8 +221,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmPara
     lrow[i] = (uint32_t)row * rowg;
     lk[i] = ((slot % CPR) ^ swz(row)) * 8;
   }
-  // loads I0 .. I1-1 of slab `slab` into `stage` (A's for q < NLA, then W's)
-  auto issue = [&](int slab, int stage, auto i0_tag, auto i1_tag) __attribute__((always_inline)) {
+  // loads I0 .. I1-1 of slab `slab` (A's for q < NLA, into A stage `stage`;
+  // then W's, into W stage `wstage`, by default `stage`)
+  auto issue = [&](int slab, int stage, auto i0_tag, auto i1_tag, int wstage = -1) __attribute__((always_inline)) {
     constexpr int I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value;
     const int k0 = slab * BK;
     static_for<I0, I1>([&](auto it) {
@@ -234,8 +235,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmPara
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(abuf(stage) + (i * kWaves + wave) * 1024), 16, off,
                                                  0, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(wbuf(stage) + (i * kWaves + wave) * 1024), 16, off,
-                                                 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(wbuf(wstage < 0 ? stage : wstage) + (i * kWaves + wave) * 1024),
+                                                 16, off, 0, 0, 0);
     });
   };
 
@@ -271,75 +272,86 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmPara
       for (int bm = 0; bm < NB; ++bm) acc[bn][bm] = mfma_32x32x16<BF16>(wf[bn], af[bm], acc[bn][bm]);
   };
 
-  constexpr int NF = 2 * NB;  // fragment reads per k-step
+  constexpr int NF = 2 * NB;   // fragment reads per k-step
   constexpr int NM = NB * NB;  // products per k-step
-  constexpr int NH = NM / 2;
-  constexpr int NL2 = NL - NL1;
-  // one fragment read after every other product of a k-step
-  auto spread_reads = [&]() __attribute__((always_inline)) {
+  constexpr int NP = NM / 2;   // products of the last k-step after the barrier
+  constexpr int NLA1 = 2;      // A loads of a slab issued after the barrier two steps ahead
+  // the order of one k-step: a fragment read after every other product,
+  // NR loads spread evenly over the products
+  auto kstep_order = [&](auto nr_tag) __attribute__((always_inline)) {
+    constexpr int NR = decltype(nr_tag)::value;
     static_for<0, NM>([&](auto it) {
       constexpr int i = decltype(it)::value;
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       if constexpr (i % 2 == 1 && i / 2 < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      if constexpr (i * NR / NM != (i + 1) * NR / NM) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
     });
   };
   u32x4 w0[NB], a0[NB], w1[NB], a1[NB];
 
-  // step j: slab j in stage ST (passed at compile time).  On entry the
-  // k-step-0 fragments of slab j are in w0/a0 and the first NL1 loads of
-  // slab j+1 are in flight.
-  auto step = [&](int j, auto st_tag) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_tag)::value;
-    const char* at = abuf(ST);
-    const char* wt = wbuf(ST);
-    // k-step 0, with the k-step-1 reads and the rest of slab j+1's loads
-    issue(j + 1, ST ^ 1, Int<NL1>{}, Int<NL>{});
+  // step j: A slab j in stage SA = j % 2, W slab j in stage SW = j % 3
+  // (passed at compile time).  On entry the k-step-0 fragments of slab j
+  // are in w0/a0, and W slab j+1 and the first NLA1 loads of A slab j+1 are
+  // in flight, in that order.
+  auto step = [&](int j, auto sa_tag, auto sw_tag) __attribute__((always_inline)) {
+    constexpr int SA = decltype(sa_tag)::value, SW = decltype(sw_tag)::value;
+    constexpr int SW2 = (SW + 2) % 3;  // W stage of slab j-1, read by every wave before the last barrier
+    const char* at = abuf(SA);
+    const char* wt = wbuf(SW);
+    // k-step 0, with the rest of A slab j+1's loads
+    issue(j + 1, SA ^ 1, Int<NLA1>{}, Int<NLA>{});
     read(w1, a1, wt, at, 1);
     mm(w0, a0, 0, NB);
-    static_for<0, NM>([&](auto it) {
-      constexpr int i = decltype(it)::value;
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if constexpr (i % 2 == 1 && i / 2 < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      if constexpr (i * NL2 / NM != (i + 1) * NL2 / NM) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
-    });
+    kstep_order(Int<NLA - NLA1>{});
+    // k-steps 1 and 2, with W slab j+2's loads (after every A load of slab
+    // j+1, so that the wait below can leave them in flight)
     read(w0, a0, wt, at, 2);
+    issue(j + 2, 0, Int<NLA>{}, Int<NLA + NLA / 2>{}, SW2);
     mm(w1, a1, 0, NB);
-    spread_reads();
+    kstep_order(Int<NLA / 2>{});
     read(w1, a1, wt, at, 3);
+    issue(j + 2, 0, Int<NLA + NLA / 2>{}, Int<NL>{}, SW2);
     mm(w0, a0, 0, NB);
-    spread_reads();
-    // k-step 3: half of the products, then the wait for slab j+1 (the only
-    // loads in flight: every later slab is issued after this point) and the
-    // barrier after which every wave has read all of slab j, whose stage
-    // then takes the first loads of slab j+2
+    kstep_order(Int<NLA - NLA / 2>{});
+    // k-step 3: half of the products, then the wait for slab j+1 (only W
+    // slab j+2's loads, the last issued, stay in flight) and the barrier
+    // after which every wave has read all of A slab j: its stage takes the
+    // first loads of A slab j+2 while the rest of the products cover the
+    // reads of slab j+1's first fragments
     mm(w1, a1, 0, NB / 2);
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NLA) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    read(w0, a0, wbuf(ST ^ 1), abuf(ST ^ 1), 0);
-    issue(j + 2, ST, Int<0>{}, Int<NL1>{});
+    read(w0, a0, wbuf((SW + 1) % 3), abuf(SA ^ 1), 0);
+    issue(j + 2, SA, Int<0>{}, Int<NLA1>{});
     mm(w1, a1, NB / 2, NB);
-    static_for<0, NH>([&](auto it) {
+    static_for<0, NP>([&](auto it) {
       constexpr int i = decltype(it)::value;
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if constexpr (i < NF) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      if constexpr (i * NL1 / NH != (i + 1) * NL1 / NH)
-        __builtin_amdgcn_sched_group_barrier(kSchedVmem, (i + 1) * NL1 / NH - i * NL1 / NH, 0);
+      if constexpr (i * NF / NP != (i + 1) * NF / NP)
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (i + 1) * NF / NP - i * NF / NP, 0);
+      if constexpr (i * NLA1 / NP != (i + 1) * NLA1 / NP)
+        __builtin_amdgcn_sched_group_barrier(kSchedVmem, (i + 1) * NLA1 / NP - i * NLA1 / NP, 0);
     });
   };
 
   const int nk = (p.K + BK - 1) / BK;
+  // prologue: slab 0, then W slab 1, then A slab 1's first loads
   issue(0, 0, Int<0>{}, Int<NL>{});
-  issue(1, 1, Int<0>{}, Int<NL1>{});
-  // slab 0 has landed once only slab 1's first loads are in flight
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NL1) : "memory");
+  issue(1, 0, Int<NLA>{}, Int<NL>{}, 1);
+  issue(1, 1, Int<0>{}, Int<NLA1>{});
+  // slab 0 has landed once only slab 1's loads are in flight
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NLA + NLA1) : "memory");
   read(w0, a0, wbuf(0), abuf(0), 0);
   int j = 0;
-  for (; j + 2 <= nk; j += 2) {
-    step(j, Int<0>{});
-    step(j + 1, Int<1>{});
-  }
-  if (j < nk) step(j, Int<0>{});
+  for (; j + 6 <= nk; j += 6) static_for<0, 6>([&](auto it) {
+    constexpr int i = decltype(it)::value;
+    step(j + i, Int<i % 2>{}, Int<i % 3>{});
+  });
+  static_for<0, 5>([&](auto it) {
+    constexpr int i = decltype(it)::value;
+    if (j + i < nk) step(j + i, Int<i % 2>{}, Int<i % 3>{});
+  });
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // epilogue: lane holds C[m][n] for m = m0 + 128 wm + 32 bm + l%32 and
