@@ -103,6 +103,7 @@ constexpr int kBM = 32 * kWaves;                // queries per work-group (one k
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmem = 0x010;
 constexpr int kSchedDsRead = 0x100;
 
 struct Params {
@@ -626,12 +627,24 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     // one, so a SIMD's other wave, in the middle of its step, issues first
     // (measured: +0.5%)
     __builtin_amdgcn_s_setprio(1);
-    issue_k(j + 5, kbuf((jm + 1) & 3));
-    issue_v(j + 3, vbuf((jm + 3) & 3));
+    // D = 128: the step's loads go between its products (below), so that
+    // the waves of a CU do not all fill the address unit's queue at once
+    // after the barrier (measured: +1-2% at D = 128, -0.3% at D = 64)
+    constexpr int NLS = 2 * NLD;  // loads per step
+    constexpr int NMF = NS + NU * DB + NU;  // matrix instructions per step
+    constexpr int LSP = D == 128 ? (NMF / NLS >= 4 ? 4 : NMF / NLS) : 0;  // products per load
+    if constexpr (LSP == 0) {
+      issue_k(j + 5, kbuf((jm + 1) & 3));
+      issue_v(j + 3, vbuf((jm + 3) & 3));
+    }
     const char* kt = kbuf((jm + 2) & 3);
     const char* vt = vbuf(jm);
 
     if (redo) reref(snext, pcur, scur);  // (snext still holds the scores of tile j)
+    if constexpr (LSP != 0) {
+      issue_k(j + 5, kbuf((jm + 1) & 3));
+      issue_v(j + 3, vbuf((jm + 3) & 3));
+    }
     tile_exp(scur, pnext, Flag<false>{});
     // the first NPF K fragments of tile j+2 were read by the previous step
 #pragma unroll
@@ -648,7 +661,6 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
       // vector instructions and two LDS reads (the first K fragments are read up front); the vector
       // work (per 16-key slice 8 multiplies, 8 exponentials and 4 packs)
       // is spread over most of the step
-      constexpr int NMF = NS + NU * DB + NU;
       constexpr int VPM = D == 64 ? 3 : 2;
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
@@ -656,6 +668,8 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedValu, VPM, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        if constexpr (LSP != 0)
+          if (i % LSP == LSP - 1 && i / LSP < NLS) __builtin_amdgcn_sched_group_barrier(kSchedVmem, 1, 0);
       }
     }
     // K fragments of tile j+3 for the next step
