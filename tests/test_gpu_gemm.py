@@ -90,6 +90,12 @@ SHAPES = [
     (1000, 130, 264, "bf16", True),
     (77, 1030, 40, "f16", True),        # N not a multiple of 4: element stores
     (513, 64, 2048, "bf16", True),
+    # K slab counts (64 wide) around the six-slab unroll: 3, 4, 6, 7, 13
+    (260, 300, 136, "f16", True),
+    (256, 256, 256, "bf16", True),
+    (200, 520, 384, "bf16", False),
+    (300, 256, 392, "f16", True),
+    (129, 130, 776, "bf16", True),
 ]
 
 

@@ -47,7 +47,9 @@
 //    the 32 tiles an XCD runs together are 4 rows by 8 columns of tiles, and
 //    share rows of A and W in its L2.
 //  * Epilogue: acc + bias[n] (read after the K loop), gelu in fp32 with the
-//    Abramowitz-Stegun erf approximation, rounded to nearest even.
+//    Abramowitz-Stegun erf approximation, rounded to nearest even, staged
+//    through the (then idle) LDS stages so that C is written in whole
+//    cache lines.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -381,6 +383,48 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmPara
         bias_pk[bn][g] = v;
       }
   }
+  if ((p.N & 7) == 0) {
+    // rows of C that are whole 16-byte chunks: every wave has read all of
+    // the stages, so each takes one 32 KiB stage array for its 128 x 128
+    // tile of C (rows of 256 bytes, 16-byte chunk c at c ^ (row & 15), so
+    // that both the writes of 32 rows at one chunk and the reads of 4 whole
+    // rows are free of bank conflicts) and stores it as whole rows: 16-byte
+    // stores covering full 128-byte lines, marked non-temporal as C is not
+    // read again.  (Stored straight from the accumulators, each store wrote
+    // 16 bytes into each of 32 rows.)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    char* ct = reinterpret_cast<char*>(wave == 0 ? as0 : wave == 1 ? as1 : wave == 2 ? ws0 : ws1);
+#pragma unroll
+    for (int bm = 0; bm < NB; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < NB; ++bn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint16_t bh = (uint16_t)(bias_pk[bn][g][e >> 1] >> (16 * (e & 1)));
+            y[e] = gelu(acc[bn][bm][4 * g + e] + to_f32<BF16>(bh));
+          }
+          u32x2 v;
+          v[0] = pack2<BF16>(y[0], y[1]);
+          v[1] = pack2<BF16>(y[2], y[3]);
+          const int r = bm * 32 + fr, cc = bn * 4 + g;
+          *reinterpret_cast<u32x2*>(ct + r * 256 + ((cc ^ (r & 15)) << 4) + fh * 8) = v;
+        }
+#pragma unroll
+    for (int i = 0; i < WT * WT * 2 / 1024; ++i) {
+      const int lin = i * 64 + lane;
+      const int r = lin >> 4, cc = lin & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ct + r * 256 + ((cc ^ (r & 15)) << 4));
+      const int m = m0 + wm * WT + r, n = n0 + wn * WT + cc * 8;
+      if (m < p.M && n < p.N) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.c + (size_t)m * p.N + n));
+    }
+    return;
+  }
+  // otherwise straight from the accumulators
   const bool vec = (p.N & 3) == 0;
 #pragma unroll
   for (int bm = 0; bm < NB; ++bm) {
