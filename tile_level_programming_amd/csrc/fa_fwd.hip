@@ -829,6 +829,41 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
       }
     if (h == 0) p.plse[row] = l == 0.f ? -INFINITY : (m_ref * c + __log2f(l + l_corr)) * kLn2;
   }
+  if constexpr (!SPLIT && KG == 1) {
+    // O through the LDS, so that it is stored in whole rows (16-byte stores
+    // that complete 128-byte lines) rather than 16 bytes into each of 32
+    // rows per store: every wave has read all of the stages, and each writes
+    // its 32 rows of O into its own K stage, 16-byte chunk cc of row r at
+    // cc ^ f(r), which keeps both the writes (32 rows at one chunk) and the
+    // reads (whole rows) free of bank conflicts (measured: +1-1.4% at
+    // D = 128, unchanged at D = 64)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    char* ob = kbuf(wave);
+    auto osw = [](int r) __attribute__((always_inline)) { return D == 64 ? ((r >> 1) & 7) : (r & 15); };
+    const float inv = 1.f / l_run;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        u32x2 w;
+        w[0] = pack2<BF16>(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv);
+        w[1] = pack2<BF16>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
+        const int cc = db * 4 + gq;  // the chunk of d = 32 db + 8 gq + 4 h .. +3
+        *reinterpret_cast<u32x2*>(ob + n * ROWB + ((cc ^ osw(n)) << 4) + h * 8) = w;
+      }
+    if (qi < p.Sq && h == 0) p.lse[(size_t)bh * p.Sq + qi] = (m_ref * c + __log2f(l_run + l_corr)) * kLn2;
+    uint16_t* og = p.o + ((size_t)bh * p.Sq + qw0) * D;
+#pragma unroll
+    for (int i = 0; i < 32 * ROWB / 1024; ++i) {
+      const int lin = i * 64 + lane;
+      const int r = lin / CH, cc = lin % CH;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ob + r * ROWB + ((cc ^ osw(r)) << 4));
+      if (qw0 + r < p.Sq) *reinterpret_cast<u32x4*>(og + r * D + cc * 8) = v;
+    }
+    return;
+  }
   if (!SPLIT && qw0 < p.Sq) {
     const float l = l_run;
     if (qi < p.Sq) {
