@@ -40,8 +40,9 @@
 //    stage during the middle k-steps of step j, a whole step before it is
 //    needed.
 //  * Rows past M or N lie outside the buffer range and read as zeros;
-//    chunks past K get an offset outside the range and read as zeros.
-//    Slabs past the end are loaded as zeros too.
+//    slabs past the end go through a resource with an empty range; when K
+//    is not a multiple of 64, chunks past K get an offset outside the range
+//    (both read as zeros and touch no memory).
 //  * Work-group ids are remapped so that each XCD runs a contiguous range of
 //    tiles, ordered in groups of 4 tile rows (column-major inside a group):
 //    the 32 tiles an XCD runs together are 4 rows by 8 columns of tiles, and
@@ -176,7 +177,9 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   return base + local;
 }
 
-template <bool BF16>
+// KTAIL: K is not a multiple of BK, and the last slab's chunks past K must
+// read as zeros lane by lane
+template <bool BF16, bool KTAIL>
 __global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmParams p) {
   // one array per stage and matrix: the compiler can then tell that the
   // loads streaming into one stage never alias the reads from another
@@ -225,19 +228,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmPara
   }
   // loads I0 .. I1-1 of slab `slab` (A's for q < NLA, into A stage `stage`;
   // then W's, into W stage `wstage`, by default `stage`)
+  // A slab past the end (the last steps load two) goes through a resource
+  // with an empty range: its loads read zeros and touch no memory.  With
+  // K a multiple of BK that uniform choice is the only check; otherwise
+  // each lane also checks its chunk against K.
+  const __amdgpu_buffer_rsrc_t rnone = __builtin_amdgcn_make_buffer_rsrc((void*)p.a, (short)0, 0u, kBufferWord3);
   auto issue = [&](int slab, int stage, auto i0_tag, auto i1_tag, int wstage = -1) __attribute__((always_inline)) {
     constexpr int I0 = decltype(i0_tag)::value, I1 = decltype(i1_tag)::value;
     const int k0 = slab * BK;
+    const bool live = k0 < p.K;
+    const __amdgpu_buffer_rsrc_t rA = live ? ra : rnone, rW = live ? rw : rnone;
     static_for<I0, I1>([&](auto it) {
       constexpr int q = decltype(it)::value;
       constexpr int i = q % NLA;
       const int k = k0 + lk[i];
-      const uint32_t off = k < p.K ? lrow[i] + (uint32_t)k * 2u : kOutOfRange;
+      uint32_t off = lrow[i] + (uint32_t)k * 2u;
+      if constexpr (KTAIL) off = k < p.K ? off : kOutOfRange;
       if constexpr (q < NLA)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(abuf(stage) + (i * kWaves + wave) * 1024), 16, off,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(abuf(stage) + (i * kWaves + wave) * 1024), 16, off,
                                                  0, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(wbuf(wstage < 0 ? stage : wstage) + (i * kWaves + wave) * 1024),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void*)(wbuf(wstage < 0 ? stage : wstage) + (i * kWaves + wave) * 1024),
                                                  16, off, 0, 0, 0);
     });
   };
@@ -495,8 +506,11 @@ extern "C" fa_status gemm_bias_gelu(const void* a, const void* w, const void* bi
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   void* args[] = {&p};
-  const void* fn = dtype == FA_BF16 ? reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<true>)
-                                    : reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<false>);
+  const bool ktail = K % BK != 0;
+  const void* fn = dtype == FA_BF16 ? (ktail ? reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<true, true>)
+                                             : reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<true, false>))
+                                    : (ktail ? reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<false, true>)
+                                             : reinterpret_cast<const void*>(&gemm_bias_gelu_kernel<false, false>));
   const hipError_t err = hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * kWaves), args, 0,
                                          static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
