@@ -214,20 +214,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmPara
       (void*)(p.w + (size_t)n0 * p.K), (short)0, (uint32_t)min(BN, p.N - n0) * rowg, kBufferWord3);
 
   // load slots: load i of a matrix fills 1 KiB block i * kWaves + wave of
-  // its slab; lane l writes bytes 16l .. 16l + 15 of it: row slot / CPR,
-  // physical chunk slot % CPR, which holds logical chunk pc ^ swz(row).
-  // The slots are the same for A and W.
-  uint32_t lrow[NLA];
-  int lk[NLA];
-#pragma unroll
-  for (int i = 0; i < NLA; ++i) {
-    const int slot = (i * kWaves + wave) * 64 + lane;
-    const int row = slot / CPR;
-    lrow[i] = (uint32_t)row * rowg;
-    lk[i] = ((slot % CPR) ^ swz(row)) * 8;
-  }
-  // loads I0 .. I1-1 of slab `slab` (A's for q < NLA, into A stage `stage`;
-  // then W's, into W stage `wstage`, by default `stage`)
+  // its slab; lane l writes bytes 16l .. 16l + 15 of it, that is row
+  // 32i + 8 wave + l/8, physical chunk l % 8, which holds logical chunk
+  // (l % 8) ^ swz(row) = (l % 8) ^ (4 (wave & 1) + l / 16): the same chunk
+  // for every i (32i + 8 wave moves swz by a multiple of 8 rows), so one
+  // offset per lane serves every load of A and W.
+  static_assert(kWaves == 4 && CPR == 8, "the slot formula assumes four waves and 8 chunks per row");
+  const int lk = ((lane & 7) ^ ((wave & 1) * 4 + (lane >> 4))) * 8;  // the lane's k within a slab
+  const uint32_t lbase = (uint32_t)(wave * 8 + (lane >> 3)) * rowg + (uint32_t)lk * 2u;
   // A slab past the end (the last steps load two) goes through a resource
   // with an empty range: its loads read zeros and touch no memory.  With
   // K a multiple of BK that uniform choice is the only check; otherwise
@@ -238,12 +232,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gemm_bias_gelu_kernel(GemmPara
     const int k0 = slab * BK;
     const bool live = k0 < p.K;
     const __amdgpu_buffer_rsrc_t rA = live ? ra : rnone, rW = live ? rw : rnone;
+    const bool lane_in = !KTAIL || k0 + lk < p.K;
     static_for<I0, I1>([&](auto it) {
       constexpr int q = decltype(it)::value;
       constexpr int i = q % NLA;
-      const int k = k0 + lk[i];
-      uint32_t off = lrow[i] + (uint32_t)k * 2u;
-      if constexpr (KTAIL) off = k < p.K ? off : kOutOfRange;
+      uint32_t off = lbase + ((uint32_t)(i * 32) * rowg + (uint32_t)k0 * 2u);
+      if constexpr (KTAIL) off = lane_in ? off : kOutOfRange;
       if constexpr (q < NLA)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(abuf(stage) + (i * kWaves + wave) * 1024), 16, off,
                                                  0, 0, 0);
