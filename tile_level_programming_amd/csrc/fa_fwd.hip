@@ -916,14 +916,14 @@ hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream
       p.n_qblk = (int)((Sq + kBM / 2 - 1) / (kBM / 2));
       p.n_wg = (int)(BH * p.n_qblk);
     }
-  // Causal blocks run longest first across an XCD's heads when a head has
-  // fewer query blocks than the XCD (32 CUs) has work-group slots: head by
-  // head, the long blocks of the XCD's last heads would start late
-  // (simulated: 1.21x the balanced time at 32 blocks on 64 slots, measured
-  // +9% on B4 H16 S4096 D128).  With more blocks per head than slots the
-  // head-by-head order is balanced already and keeps fewer heads' keys in
-  // the XCD's L2 (measured 1.3% faster at 128 blocks on 64 slots).
-  p.xcd_heads = (CAUSAL && !SPLIT && BH % 8 == 0 && p.n_qblk < 32 * per_cu) ? (int)(BH / 8) : 0;
+  // Causal blocks run longest first across an XCD's heads (when the heads
+  // split evenly over the 8 XCDs): head by head, the long blocks of the
+  // XCD's last heads would start late (simulated: 1.21x the balanced time
+  // at 32 blocks on 64 slots, measured +9% on B4 H16 S4096 D128).  With more
+  // blocks per head than slots it still measured +1.0% (B1 H32 S16384
+  // D128, 128 blocks on 64 slots), though fewer heads' keys then share the
+  // XCD's L2 at a time in the head-by-head order.
+  p.xcd_heads = (CAUSAL && !SPLIT && BH % 8 == 0) ? (int)(BH / 8) : 0;
   void* args[] = {&p};
   return hipLaunchKernel(fn, dim3(p.n_wg), dim3(64 * kWaves), args, 0, stream);
 }
