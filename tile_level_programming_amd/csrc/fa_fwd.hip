@@ -267,7 +267,7 @@ struct Int { static constexpr int value = I; };
 // work-group owns 32*kWaves/KG queries.  The longest block's work is then
 // spread over KG times as many work-groups, each SIMD doing 1/KG of it.
 template <int D, bool BF16, bool CAUSAL, int BN, bool SPLIT, int KG = 1>
-__global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kernel(Params p) {
+__global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kernel(Params p) {
   constexpr int WPG = kWaves / KG;                // waves per key group
   constexpr int BM = 32 * WPG;                    // queries per work-group
   constexpr int CH = D / 8;                       // 16-byte chunks per row
@@ -310,6 +310,13 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
   auto vbuf = [&](int t) __attribute__((always_inline)) -> char* {
     return reinterpret_cast<char*>(t == 0 ? vst0 : t == 1 ? vst1 : t == 2 ? vst2 : vst3) + grp * TILE;
   };
+  // The fragment reads of stage t.  With two key groups they take the stage's
+  // base (a constant, which the LDS reads carry as their immediate offset)
+  // and the group's offset sits in the per-lane offsets koff and voff: a
+  // runtime base per stage would cost a register per stage and fragment.
+  constexpr int GOFF = KG > 1 ? TILE : 0;  // per-lane offset of group 1's tiles
+  auto krd = [&](int t) __attribute__((always_inline)) -> const char* { return kbuf(t) - grp * GOFF; };
+  auto vrd = [&](int t) __attribute__((always_inline)) -> const char* { return vbuf(t) - grp * GOFF; };
   const int n = lane & 31;  // query column owned by this lane
   const int h = lane >> 5;  // which half of the wave
 
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
   // K (A operand of S^T): row 32*kb + n, logical chunk 2*ks + h.
   int koff[DK];
 #pragma unroll
-  for (int ks = 0; ks < DK; ++ks) koff[ks] = n * ROWB + (((2 * ks + h) ^ ksw<D>(n)) << 4);
+  for (int ks = 0; ks < DK; ++ks) koff[ks] = grp * GOFF + n * ROWB + (((2 * ks + h) ^ ksw<D>(n)) << 4);
   // V (A operand of O^T through the transposing read): in 16-lane group g
   // (lane = 16g + s) source lane s points at row 4*(g/2) + s/4 (+ 16u + 8*half)
   // and element 32*db + 16*(g%2) + 4*(s%4); the lane then receives
@@ -430,7 +437,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int chunk = 4 * db + 2 * (g & 1) + ((s & 3) >> 1);
-    voff[db] = vrow * ROWB + ((chunk ^ vsw<D>(vrow)) << 4) + ((s & 1) << 3);
+    voff[db] = grp * GOFF + vrow * ROWB + ((chunk ^ vsw<D>(vrow)) << 4) + ((s & 1) << 3);
   }
 
   // ---- running state of this lane's query
@@ -637,8 +644,8 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
       issue_k(j + 5, kbuf((jm + 1) & 3));
       issue_v(j + 3, vbuf((jm + 3) & 3));
     }
-    const char* kt = kbuf((jm + 2) & 3);
-    const char* vt = vbuf(jm);
+    const char* kt = krd((jm + 2) & 3);
+    const char* vt = vrd(jm);
 
     if (redo) reref(snext, pcur, scur);  // (snext still holds the scores of tile j)
     if constexpr (LSP != 0) {
@@ -674,7 +681,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     }
     // K fragments of tile j+3 for the next step
 #pragma unroll
-    for (int i = 0; i < NPF; ++i) kpre[i] = k_frag(kbuf((jm + 3) & 3), i);
+    for (int i = 0; i < NPF; ++i) kpre[i] = k_frag(krd((jm + 3) & 3), i);
     // pin the packed P to this block: the packing would otherwise sink past
     // the next step's redo branch, out of the interleaved schedule
 #pragma unroll
@@ -692,8 +699,8 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     issue_k(j + 5, kbuf((j + 5) & 3));
     issue_v(j + 3, vbuf((j + 3) & 3));
     if (j < nt_w) {
-      const char* kt = kbuf((j + 2) & 3);
-      const char* vt = vbuf(j & 3);
+      const char* kt = krd((j + 2) & 3);
+      const char* vt = vrd(j & 3);
       if (redo) reref(snext, pcur, scur);
       if (j + 2 < nt_w) score_tile(snext, kt);
       float ts = 0.f, td = 0.f;
@@ -726,7 +733,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     // the range at all (a split with i < kb0): that row keeps a zero
     // reference, its P are all 0 and its sum stays 0.
     set_negm();
-    score_tile(sa, kbuf(0));
+    score_tile(sa, krd(0));
     apply_mask(sa, 0);
     m_ref = tile_max(sa);
     if ((SPLIT || KG > 1) && CAUSAL && m_ref == -INFINITY) m_ref = 0.f;
@@ -738,7 +745,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
     const Sums t0 = tile_exp(sa, pa, Flag<true>{});
     l_run = sum_halves(t0.r);
     l_corr = sum_halves(t0.d);
-    score_tile(sb, kbuf(1));
+    score_tile(sb, krd(1));
   }
 
   // step j: scores of tile j+1 in sb (j even) or sa (j odd), P of tile j in
@@ -746,7 +753,7 @@ __global__ __launch_bounds__(256, D == 64 && BN == 32 ? 3 : 2) void fa_fwd_kerne
   int j = 0;
   if (j_fast > 0) {
 #pragma unroll
-    for (int i = 0; i < NPF; ++i) kpre[i] = k_frag(kbuf(2), i);
+    for (int i = 0; i < NPF; ++i) kpre[i] = k_frag(krd(2), i);
   }
   // every wave's reads of K tile 0 were consumed by its prologue products:
   // the stage can take K tile 4
@@ -903,16 +910,11 @@ hipError_t launch(const Params& base, int64_t BH, int64_t Sq, hipStream_t stream
   p.n_qblk = (int)((Sq + kBM - 1) / kBM);
   p.n_wg = (int)(BH * p.n_qblk * p.n_split);
   const void* fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, 32, SPLIT>);
-  int per_cu = D == 64 ? 3 : 2;  // work-groups resident per CU
   if constexpr (D == 64)
-    if (p.n_wg <= kSmallGrid) {
-      fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, 64, SPLIT>);
-      per_cu = 2;
-    }
+    if (p.n_wg <= kSmallGrid) fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, 64, SPLIT>);
   if constexpr (!SPLIT)
     if (p.n_wg <= kHalfGrid) {
       fn = reinterpret_cast<const void*>(&fa_fwd_kernel<D, BF16, CAUSAL, D == 64 ? 64 : 32, SPLIT, 2>);
-      per_cu = 1;
       p.n_qblk = (int)((Sq + kBM / 2 - 1) / (kBM / 2));
       p.n_wg = (int)(BH * p.n_qblk);
     }
