@@ -315,8 +315,14 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
   // and the group's offset sits in the per-lane offsets koff and voff: a
   // runtime base per stage would cost a register per stage and fragment.
   constexpr int GOFF = KG > 1 ? TILE : 0;  // per-lane offset of group 1's tiles
-  auto krd = [&](int t) __attribute__((always_inline)) -> const char* { return kbuf(t) - grp * GOFF; };
-  auto vrd = [&](int t) __attribute__((always_inline)) -> const char* { return vbuf(t) - grp * GOFF; };
+  auto krd = [&](int t) __attribute__((always_inline)) -> const char* {
+    if constexpr (KG == 1) return kbuf(t);
+    else return reinterpret_cast<const char*>(t == 0 ? kst0 : t == 1 ? kst1 : t == 2 ? kst2 : kst3);
+  };
+  auto vrd = [&](int t) __attribute__((always_inline)) -> const char* {
+    if constexpr (KG == 1) return vbuf(t);
+    else return reinterpret_cast<const char*>(t == 0 ? vst0 : t == 1 ? vst1 : t == 2 ? vst2 : vst3);
+  };
   const int n = lane & 31;  // query column owned by this lane
   const int h = lane >> 5;  // which half of the wave
 
@@ -404,6 +410,16 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
   // read ahead), V 0, K 3, V 1, V 2; K 4 goes into K 0's stage once every
   // wave has read K 0.  Every step issues 2*NLD loads, past the keys
   // included, so each wait has a fixed count.
+  // ---- Q fragments: B operands of S^T = K Q^T; lane holds q[qi][16*ks + 8*h .. +8].
+  // Loaded before the tiles: the load counter drains in order, so Q issued
+  // after them would wait for every tile of the prologue.  Every lane loads
+  // (rows past the queries read the last row, Sq >= 1) and those rows are
+  // zeroed once the tiles are issued: a load under a branch per lane let
+  // the compiler wait for it inside the branch, before the tiles went out.
+  u32x4 qf[DK];
+  const int qrow = min(qi, p.Sq - 1);
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qg + (size_t)qrow * D + ks * 16 + h * 8);
   issue_k(0, kbuf(0));
   issue_k(1, kbuf(1));
   issue_k(2, kbuf(2));
@@ -411,16 +427,8 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
   issue_k(3, kbuf(3));
   issue_v(1, vbuf(1));
   issue_v(2, vbuf(2));
-
-  // ---- Q fragments: B operands of S^T = K Q^T; lane holds q[qi][16*ks + 8*h .. +8]
-  u32x4 qf[DK];
 #pragma unroll
-  for (int ks = 0; ks < DK; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < p.Sq) x = *reinterpret_cast<const u32x4*>(qg + (size_t)qi * D + ks * 16 + h * 8);
-    x ^= p.qsign;
-    qf[ks] = x;
-  }
+  for (int ks = 0; ks < DK; ++ks) qf[ks] = qi < p.Sq ? (qf[ks] ^ p.qsign) : u32x4{0u, 0u, 0u, 0u};
 
   // ---- per-lane fragment read offsets (bytes within a tile)
   // K (A operand of S^T): row 32*kb + n, logical chunk 2*ks + h.
@@ -692,15 +700,23 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
   };
 
   // Any step: the tiles may need masks, and tile j+1 or j+2 may not exist
-  // for this wave.
-  auto step_any = [&](int j, f32x16* scur, f32x16* snext, u32x4* pcur, u32x4* pnext) __attribute__((always_inline)) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD) : "memory");
-    __syncthreads();
-    issue_k(j + 5, kbuf((j + 5) & 3));
-    issue_v(j + 3, vbuf((j + 3) & 3));
+  // for this wave.  Its stages are compile-time too (jm = j % 4): with a
+  // stage chosen at run time the compiler cannot tell which stage the loads
+  // in flight write, and waits for all of them before the step's LDS reads.
+  auto step_any = [&](int j, auto jm4_tag, f32x16* scur, f32x16* snext, u32x4* pcur,
+                      u32x4* pnext) __attribute__((always_inline)) {
+    constexpr int jm = decltype(jm4_tag)::value;  // j % 4
+    // the same wait and barrier as a branch-free step (and the same
+    // argument): a fence here would also wait for the loads of the previous
+    // step, which have had one step to land instead of two
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NLD) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue_k(j + 5, kbuf((jm + 1) & 3));
+    issue_v(j + 3, vbuf((jm + 3) & 3));
     if (j < nt_w) {
-      const char* kt = krd((j + 2) & 3);
-      const char* vt = vrd(j & 3);
+      const char* kt = krd((jm + 2) & 3);
+      const char* vt = vrd(jm);
       if (redo) reref(snext, pcur, scur);
       if (j + 2 < nt_w) score_tile(snext, kt);
       float ts = 0.f, td = 0.f;
@@ -725,8 +741,11 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
   // ---- prologue: scores of tiles 0 and 1, P of tile 0
   f32x16 sa[KB], sb[KB];
   u32x4 pa[NU], pb[NU];
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NLD) : "memory");  // K 0, K 1 and K 2 have landed
-  __syncthreads();
+  // K 0, K 1 and K 2 have landed (in every wave: the barrier); the loads
+  // after them may stay in flight (no fence)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(4 * NLD) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
   if (nt_w > 0) {
     // tile 0 from a zero reference; its row maximum becomes the reference.
     // Key 0 of the range is masked only for a causal row that sees no key of
@@ -767,10 +786,13 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
     step_fast(j + 2, Int<2>{}, sb, sa, pa, pb);
     step_fast(j + 3, Int<3>{}, sa, sb, pb, pa);
   }
-  // (j is a multiple of 4 here)
-  for (; j < nsteps; j += 2) {
-    step_any(j, sb, sa, pa, pb);
-    if (j + 1 < nsteps) step_any(j + 1, sa, sb, pb, pa);
+  // (j is a multiple of 4 here; the conditions are the same for every wave
+  // of the work-group, so every wave meets every barrier)
+  for (; j < nsteps; j += 4) {
+    step_any(j, Int<0>{}, sb, sa, pa, pb);
+    if (j + 1 < nsteps) step_any(j + 1, Int<1>{}, sa, sb, pb, pa);
+    if (j + 2 < nsteps) step_any(j + 2, Int<2>{}, sb, sa, pa, pb);
+    if (j + 3 < nsteps) step_any(j + 3, Int<3>{}, sa, sb, pb, pa);
   }
 
   // the last steps' loads (past the keys) are still in flight: let them land
