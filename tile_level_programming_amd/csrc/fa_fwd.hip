@@ -313,7 +313,9 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
   // The fragment reads of stage t.  With two key groups they take the stage's
   // base (a constant, which the LDS reads carry as their immediate offset)
   // and the group's offset sits in the per-lane offsets koff and voff: a
-  // runtime base per stage would cost a register per stage and fragment.
+  // runtime base per stage would cost a register per stage and fragment,
+  // and would hide from the compiler which stage a read touches, so that it
+  // waited for every load in flight (they write other stages) before reads.
   constexpr int GOFF = KG > 1 ? TILE : 0;  // per-lane offset of group 1's tiles
   auto krd = [&](int t) __attribute__((always_inline)) -> const char* {
     if constexpr (KG == 1) return kbuf(t);
@@ -403,13 +405,6 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
     load_rows_to_lds<NLD>(rv, tile * BN, ROWB, buf + wave * 1024, WPG * 1024, offv);
   };
 
-  // Tile t of K lands two steps before its fragments are read (at the end of
-  // step t-3), tile t of V three steps before it is read (step t): step j
-  // issues K j+5 and V j+3, and waits for the loads of step j-2.  K 0 and
-  // K 1 come first (the prologue's scores), then K 2 (the first fragments
-  // read ahead), V 0, K 3, V 1, V 2; K 4 goes into K 0's stage once every
-  // wave has read K 0.  Every step issues 2*NLD loads, past the keys
-  // included, so each wait has a fixed count.
   // ---- Q fragments: B operands of S^T = K Q^T; lane holds q[qi][16*ks + 8*h .. +8].
   // Loaded before the tiles: the load counter drains in order, so Q issued
   // after them would wait for every tile of the prologue.  Every lane loads
@@ -420,6 +415,14 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
   const int qrow = min(qi, p.Sq - 1);
 #pragma unroll
   for (int ks = 0; ks < DK; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qg + (size_t)qrow * D + ks * 16 + h * 8);
+
+  // Tile t of K lands two steps before its fragments are read (at the end of
+  // step t-3), tile t of V three steps before it is read (step t): step j
+  // issues K j+5 and V j+3, and waits for the loads of step j-2.  K 0 and
+  // K 1 come first (the prologue's scores), then K 2 (the first fragments
+  // read ahead), V 0, K 3, V 1, V 2; K 4 goes into K 0's stage once every
+  // wave has read K 0.  Every step issues 2*NLD loads, past the keys
+  // included, so each wait has a fixed count.
   issue_k(0, kbuf(0));
   issue_k(1, kbuf(1));
   issue_k(2, kbuf(2));
