@@ -147,6 +147,32 @@ def test_wide_grid_shapes(torch_dev, fa, oracle_mod, shape, causal, dtype):
     full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(D), causal, f"{shape} {causal} {dtype}")
 
 
+# Shapes on both sides of the launch choices, which depend on the number of
+# 128-query blocks B*H*ceil(Sq/128): up to 128 run as two key groups of two
+# waves (64 queries per work-group), up to 512 (D=64) with 64-key tiles, beyond
+# with 32-key tiles.  The keys end inside a tile.
+BOUNDARY = [
+    # (B, H, Sq, Sk, D, dtype)        blocks
+    (1, 16, 1024, 1061, 64, "f16"),   # 128
+    (1, 43, 384, 421, 64, "f16"),     # 129
+    (2, 32, 1024, 1061, 64, "f16"),   # 512
+    (1, 171, 384, 421, 64, "f16"),    # 513
+    (1, 16, 1024, 1061, 128, "bf16"),  # 128
+    (1, 43, 384, 421, 128, "bf16"),   # 129
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", BOUNDARY)
+def test_launch_boundary_shapes(torch_dev, fa, oracle_mod, shape, causal):
+    B, H, Sq, Sk, D, dtype = shape
+    seed = 500 + H + Sq
+    q = fi.tensor_bits(seed, "q", (B, H, Sq, D), dtype)
+    k = fi.tensor_bits(seed, "k", (B, H, Sk, D), dtype)
+    v = fi.tensor_bits(seed, "v", (B, H, Sk, D), dtype)
+    full_check(torch_dev, fa, oracle_mod, q, k, v, dtype, 1.0 / math.sqrt(D), causal, f"{shape} {causal}")
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 1.0, 3.0])
 @pytest.mark.parametrize("causal", [False, True])
 def test_scales(torch_dev, fa, oracle_mod, scale, causal):
