@@ -56,3 +56,44 @@ def test_graph_replays_equal_eager(shape):
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o_e.view(torch.int16)), f"replay {rep}: O differs from the eager call"
         assert torch.equal(lse.view(torch.int32), l_e.view(torch.int32)), f"replay {rep}: lse differs"
+
+
+ROW_SHAPES = [
+    # (op, R, C, dtype): one row per wave group, and rows spread over the work-group
+    ("rmsnorm_silu", 4096, 512, "bf16"),
+    ("softmax", 512, 4096, "f16"),
+    ("softmax", 64, 32000, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", ROW_SHAPES)
+def test_graph_replays_equal_eager_rows(shape):
+    import torch
+
+    from tile_level_programming_amd import fa
+
+    op, R, C, dtype = shape
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    gen = torch.Generator(device="cpu").manual_seed(R + C)
+    x = torch.randn(R, C, generator=gen).to(tdt).to("cuda")
+    g = torch.randn(C, generator=gen).to(tdt).to("cuda")
+    x2 = torch.flip(x, dims=[0]).contiguous()
+
+    def call(inp, out=None):
+        return fa.softmax(inp, out=out) if op == "softmax" else fa.rmsnorm_silu_rows(inp, g, 1e-6, out=out)
+
+    print(f"[graph] {shape}", flush=True)
+    y_e = call(x)
+    torch.cuda.synchronize()
+    y = torch.full_like(x, float("nan"))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(3):
+            call(x, out=y)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        call(x2)  # eager work on other buffers between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_e.view(torch.int16)), f"replay {rep}: output differs from the eager call"
