@@ -91,6 +91,23 @@ def traffic_for(workload: str, src: str | None = None):
     return ent.get("bytes_per_launch")
 
 
+def counters_for(workload: str, src: str | None = None):
+    """Matrix-unit busy share and LDS bank conflicts per launch, from the
+    rocprofv3 counter passes of the workload's profile on this kernel source
+    (counters are not collected in the timed run), or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_sha256_16") != kernel_hash(src) or "mfma_busy_pct" not in ent:
+        return None
+    return {"mfma_busy_pct": ent["mfma_busy_pct"], "lds_bank_conflict_cycles": ent["lds_bank_conflict_cycles"],
+            "lds_active_cycles": ent["lds_active_cycles"], "lds_conflict_rate": ent["lds_conflict_rate"],
+            "source": ent.get("source")}
+
+
 # --- the host: oracle threads, CPU model -------------------------------------
 
 
@@ -490,6 +507,7 @@ def run_attention(args, w):
                             "frac_at_measured_clock": round(tflops_kernel / pk, 4) if pk else None,
                             "traffic": traffic, "kernel_ms": round(ms_kernel, 5),
                             "algorithmic_flop_per_launch": flop}
+    line["counters"] = counters_for(w.name)
     line["kernel_sha256_16"] = kernel_hash()
     if args.no_check:
         line["cpu_baseline"] = None
