@@ -116,7 +116,7 @@ struct Params {
   int n_qblk;      // query blocks per (b, h)
   int n_wg;        // total work-groups
   int xcd_heads;   // causal, no split: heads per XCD when every XCD gets whole heads, else 0
-  float c;         // |scale| * log2(e)
+  float c;         // |scale| * log2(e), at least 1e-30
   uint32_t qsign;  // 0x80008000 when scale < 0 (q is negated on load), else 0
   // split over the keys: range r holds keys r*kchunk .. min(Sk, (r+1)*kchunk)-1
   int n_split;     // ranges (1 without a split)
@@ -254,9 +254,6 @@ __device__ __forceinline__ void load_rows_to_lds(__amdgpu_buffer_rsrc_t r, int k
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * stride), 16, (int)(base + (uint32_t)off[i]),
                                              0, 0, 0);
 }
-
-template <bool B>
-struct Flag { static constexpr bool value = B; };
 
 template <int I>
 struct Int { static constexpr int value = I; };
@@ -525,16 +522,16 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
   };
 
-  // P = exp2(s*c) of the relative scores, packed to 16 bits into pout;
-  // returns this lane's sums, in fp32, of the tile's P as rounded to 16 bits
+  // P = exp2(s*c) of the relative scores, packed to 16 bits into pout (a
+  // masked score, -inf, gives exp2(-inf) = 0: c > 0 always, see fa_fwd's
+  // set-up); returns this lane's sums, in fp32, of the tile's P as rounded to 16 bits
   // (r) and of the rounding, unrounded minus rounded (d), over half of the
   // tile's keys (sum_halves gives the row's).  The branch-free steps ignore
   // them and take the rounded sums on the matrix unit (tile_sum).
   struct Sums {
     float r, d;
   };
-  auto tile_exp = [&](const f32x16* sacc, u32x4* pout, auto mask_tag) __attribute__((always_inline)) -> Sums {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto tile_exp = [&](const f32x16* sacc, u32x4* pout) __attribute__((always_inline)) -> Sums {
     float ps[2], pu[2];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -542,9 +539,7 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         const float sv = sacc[u >> 1][8 * (u & 1) + t8];
-        float pe = __builtin_amdgcn_exp2f(sv * c);
-        if constexpr (MASK) pe = (sv == -INFINITY) ? 0.f : pe;  // also covers scale == 0
-        pv[t8] = pe;
+        pv[t8] = __builtin_amdgcn_exp2f(sv * c);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -604,7 +599,7 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
       }
     const float alpha = exp2f(-delta * c);
     scale_o(alpha);
-    const Sums ts = tile_exp(st, pout, Flag<true>{});
+    const Sums ts = tile_exp(st, pout);
     l_run = l_run * alpha + sum_halves(ts.r);
     l_corr = l_corr * alpha + sum_halves(ts.d);
   };
@@ -663,7 +658,7 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
       issue_k(j + 5, kbuf((jm + 1) & 3));
       issue_v(j + 3, vbuf((jm + 3) & 3));
     }
-    tile_exp(scur, pnext, Flag<false>{});
+    tile_exp(scur, pnext);
     // the first NPF K fragments of tile j+2 were read by the previous step
 #pragma unroll
     for (int i = 0; i < NS; ++i)
@@ -725,7 +720,7 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
       float ts = 0.f, td = 0.f;
       if (j + 1 < nt_w) {
         apply_mask(scur, (j + 1) * BN);
-        const Sums t2 = tile_exp(scur, pnext, Flag<true>{});
+        const Sums t2 = tile_exp(scur, pnext);
         ts = sum_halves(t2.r);
         td = sum_halves(t2.d);
       }
@@ -764,7 +759,7 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sa[kb][r] -= m_ref;
-    const Sums t0 = tile_exp(sa, pa, Flag<true>{});
+    const Sums t0 = tile_exp(sa, pa);
     l_run = sum_halves(t0.r);
     l_corr = sum_halves(t0.d);
     score_tile(sb, krd(1));
@@ -1063,7 +1058,12 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
   p.Sk = (int)Sk;
   p.n_qblk = 0;
   p.n_wg = 0;
-  p.c = (float)(fabs((double)scale) * 1.4426950408889634);
+  // scores times c are the exponents of 2; c is at least 1e-30 so that a
+  // masked score (-inf) gives exp2(-inf) = 0 with no test in the kernel, also
+  // for scale 0 (where -inf * 0 would be NaN).  With scale 0 every other
+  // exponent is then below 2^-60 in size for any finite score under 2^39,
+  // and exp2 returns exactly 1, as for c = 0.
+  p.c = (float)fmax(fabs((double)scale) * 1.4426950408889634, 1e-30);
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
   p.n_split = 1;
   p.kchunk = (int)Sk;
