@@ -495,14 +495,15 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
 
   // Scores past the keys or (causal) above the diagonal become -inf.
   // sacc[kb][r] = score(qi, k0 + 32kb + 8(r/4) + 4h + r%4).
+  // One compare per score: key k0 + 4h + c (c = 32kb + 8(r/4) + r%4, a
+  // constant) is masked when c > min(Skl - 1, qir) - k0 - 4h.
   auto apply_mask = [&](f32x16* sacc, int k0) __attribute__((always_inline)) {
+    const int lim = (CAUSAL ? min(Skl - 1, qir) : Skl - 1) - k0 - 4 * h;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (key >= Skl || (CAUSAL && key > qir)) sacc[kb][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
   };
 
   // Row maximum of a tile's scores (this lane's query, both halves of the
@@ -719,7 +720,7 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
       if (j + 2 < nt_w) score_tile(snext, kt);
       float ts = 0.f, td = 0.f;
       if (j + 1 < nt_w) {
-        apply_mask(scur, (j + 1) * BN);
+        if (j + 1 >= j_mask) apply_mask(scur, (j + 1) * BN);
         const Sums t2 = tile_exp(scur, pnext);
         ts = sum_halves(t2.r);
         td = sum_halves(t2.d);
@@ -751,7 +752,7 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
     // reference, its P are all 0 and its sum stays 0.
     set_negm();
     score_tile(sa, krd(0));
-    apply_mask(sa, 0);
+    if (j_mask == 0) apply_mask(sa, 0);
     m_ref = tile_max(sa);
     if ((SPLIT || KG > 1) && CAUSAL && m_ref == -INFINITY) m_ref = 0.f;
     set_negm();
