@@ -720,6 +720,8 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
       if (j + 2 < nt_w) score_tile(snext, kt);
       float ts = 0.f, td = 0.f;
       if (j + 1 < nt_w) {
+        // tiles before j_mask hold only keys before the end and at or
+        // below the wave's first query: no score of theirs is masked
         if (j + 1 >= j_mask) apply_mask(scur, (j + 1) * BN);
         const Sums t2 = tile_exp(scur, pnext);
         ts = sum_halves(t2.r);
@@ -752,7 +754,7 @@ __global__ __launch_bounds__(256, KG == 2 ? 1 : D == 64 && BN == 32 ? 3 : 2) voi
     // reference, its P are all 0 and its sum stays 0.
     set_negm();
     score_tile(sa, krd(0));
-    if (j_mask == 0) apply_mask(sa, 0);
+    if (j_mask == 0) apply_mask(sa, 0);  // (as in the general steps)
     m_ref = tile_max(sa);
     if ((SPLIT || KG > 1) && CAUSAL && m_ref == -INFINITY) m_ref = 0.f;
     set_negm();
